@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark: zero-start tail replay on one MI355X.
+
+Workload (the 5% tail-replay case): 16 requests x 32 heads, d_k = d_v = 128,
+bf16 q/k/v/alpha/beta, float32 state, matched prefix m = 32768, so each request
+replays k = ceil(0.05 m) = 1639 positions from the zero state, writing the
+per-token outputs o_t and the final state.  One step = one gdn_tail_replay call
+over the whole batch (all heads of one layer); inputs are resident in HBM
+before timing starts.
+
+Reported: replayed tokens/s per layer (all heads), the roofline fraction of
+the dominant kernel (algorithmic bytes or flops per launch / its measured
+duration), and the fp64 CPU oracle timed on a bounded sample of the same
+workload on the host cores.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
+
+
+def algorithmic_bytes(token_heads: int, pairs: int, dk: int, dv: int, elem: int,
+                      with_o: bool = True) -> int:
+    """Bytes a replay must move: q, k, v, alpha, beta in; o out; final state out."""
+    per_tok = elem * (2 * dk + dv) + 2 * elem + (elem * dv if with_o else 0)
+    return token_heads * per_tok + pairs * dv * dk * 4
+
+
+def algorithmic_flops(token_heads: int, dk: int, dv: int) -> int:
+    """S k (2 d_k d_v), rank-1 update (3 d_k d_v: scale, multiply-add), S q (2 d_k d_v)."""
+    return token_heads * 7 * dk * dv
+
+
+def cpu_baseline(w, spans, budget_s: float = 15.0):
+    """Time the fp64 C oracle, as written, on a bounded sample of (request, head) pairs."""
+    import numpy as np
+    import torch
+    import oracle
+    if not oracle.c_oracle_available():
+        from oracle.build import build_c_oracle
+        build_c_oracle()
+    threads = oracle.c_oracle_threads()
+    H = w.H
+    allp = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(pairs):
+        S0s, qs, ks, vs, al, bt = [], [], [], [], [], []
+        for (b, h) in pairs:
+            p0, n = spans[b]
+            r0 = w.tok_offset[b] + (p0 - w.first_pos[b])
+            sl = slice(r0, r0 + n)
+            f = lambda t: t[sl, h].to(torch.float64).cpu().numpy()
+            S0s.append(np.zeros((w.dv, w.dk)))
+            qs.append(f(w.q)); ks.append(f(w.k)); vs.append(f(w.v))
+            al.append(f(w.alpha)); bt.append(f(w.beta))
+        t0 = time.perf_counter()
+        oracle.scan_rank1_c_batch(S0s, qs, ks, vs, al, bt, normalize_k=True, normalize_q=True)
+        return time.perf_counter() - t0, sum(spans[b][1] for (b, _) in pairs)
+
+    # calibrate on one pair per thread, then size the sample to ~budget_s of wall time
+    n0 = min(len(allp), max(1, threads))
+    dt, toks = run(allp[:n0])
+    per_pair = dt / n0 * threads  # CPU-seconds per pair
+    n = int(min(len(allp), max(n0, budget_s * threads / max(per_pair, 1e-9))))
+    n = max(threads, (n // threads) * threads) if n >= threads else n
+    n = min(n, len(allp))
+    dt, toks = run(allp[:n])
+    rate = toks / H / dt  # token-heads / H = tokens with all heads
+    return {"value": rate, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {len(allp)} (request, head) pairs, {spans[0][1]} tokens each, "
+                      f"fp64 C rank-1 oracle with OpenMP; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--kernel", choices=["auto", "recurrent", "chunked"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-output", action="store_true", help="skip o (state only)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the replay shards over (request, head) pairs "
+              "with no exchange, so a multi-GPU figure is not part of this benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_scan_amd as gdn
+    import workloads as W
+
+    gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.config(3, device=dev)
+    flags = w.flags | {"auto": 0, "recurrent": gdn.KERNEL_RECURRENT,
+                       "chunked": gdn.KERNEL_CHUNKED}[args.kernel]
+    ks = [gdn.tail_len(m, w.r_num, w.r_den) for m in w.m]
+    spans = [(m - k + 1, k) for m, k in zip(w.m, ks)]
+    tokens = sum(ks)
+    token_heads = tokens * w.H
+    pairs = w.B * w.H
+    state = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    o = None if args.no_output else torch.empty_like(w.v)
+
+    def step():
+        gdn.tail_replay(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m, w.r_num, w.r_den,
+                        first_pos=w.first_pos, flags=flags, state_out=state, o=o,
+                        want_o=o is not None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_region = region0.elapsed_time(region1)
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = ms_region / args.steps
+    kern_ms = sum(per_launch_ms) / len(per_launch_ms)
+
+    elem = 2 if w.dtype == "bf16" else 4
+    nbytes = algorithmic_bytes(token_heads, pairs, w.dk, w.dv, elem, with_o=o is not None)
+    nflops = algorithmic_flops(token_heads, w.dk, w.dv)
+    chunked = gdn.kernel_for(w.B, w.H, w.dk, w.dv, w.torch_dtype, flags) == "chunked"
+    if chunked:
+        roof = {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "alu", "achieved": nflops / (kern_ms * 1e-3) / 1e12,
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["algorithmic_bytes_per_launch"] = nbytes
+    roof["algorithmic_flops_per_launch"] = nflops
+    roof["kernel_ms"] = kern_ms
+    roof["hbm_frac"] = nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    out = {
+        "metric": "replayed tokens/s per layer (all heads)",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if chunked else "f32",
+        "data": "synthetic",
+        "config": {"workload": "tail_replay_5pct", "requests": w.B, "heads": w.H, "d_k": w.dk,
+                   "d_v": w.dv, "matched_prefix": w.m[0], "replay_ratio": "5/100",
+                   "replay_tokens": ks[0], "inputs": w.dtype, "state": "f32",
+                   "outputs": o is not None, "kernel": "chunked" if chunked else "recurrent"},
+        "roofline": roof,
+        "wall_s_timed_region": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, spans)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

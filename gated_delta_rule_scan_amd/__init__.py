@@ -1,0 +1,258 @@
+"""Python binding of libgdnreplay (Gated DeltaNet span replay on MI355X).
+
+Argument marshalling only: every step of the replay runs in the HIP kernels of
+``libgdnreplay.so`` behind the C ABI of ``include/gdnreplay.h``.  PyTorch
+supplies device memory and the current stream.  There is no fallback: if the
+shared library is missing or cannot be loaded, every call raises.
+
+Layout (see the header for the full contract):
+  q, k [rows, H, d_k], v [rows, H, d_v], alpha, beta [rows, H]  (float32 or bfloat16)
+  request b owns rows tok_offset[b]..tok_offset[b+1]-1, whose first row holds
+  the token at 1-based position first_pos[b].
+  States are float32 [B, H, d_v, d_k]; checkpoint stores [B, M, H, d_v, d_k].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "GDNError", "NORMALIZE_K", "NORMALIZE_Q", "KERNEL_RECURRENT", "KERNEL_CHUNKED",
+    "MAX_CHECKPOINTS", "library_path", "load", "version", "kernel_for", "tail_len", "select_checkpoint",
+    "tail_replay", "resume", "prefill_emit_checkpoints",
+]
+
+NORMALIZE_K = 1
+NORMALIZE_Q = 2
+KERNEL_RECURRENT = 256
+KERNEL_CHUNKED = 512
+MAX_CHECKPOINTS = 192
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdnreplay.so")
+_lib = None
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdnreplay.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with gated_delta_rule_scan_amd.build.build() "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64p, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+    shp = ctypes.POINTER(_Shape)
+    lib.gdn_version.restype = ctypes.c_char_p
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_kernel_for.argtypes = [shp]
+    lib.gdn_kernel_for.restype = ctypes.c_int32
+    lib.gdn_tail_len.argtypes = [ctypes.c_int64] * 3
+    lib.gdn_tail_len.restype = ctypes.c_int64
+    lib.gdn_select_checkpoint.argtypes = [i64p, ctypes.c_int32, ctypes.c_int64]
+    lib.gdn_select_checkpoint.restype = ctypes.c_int32
+    lib.gdn_tail_replay.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p, ctypes.c_int64,
+                                    ctypes.c_int64, vp, vp, i64p, vp]
+    lib.gdn_tail_replay.restype = ctypes.c_int
+    lib.gdn_resume.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p, ctypes.c_int32, vp,
+                               i64p, vp, vp, i32p, vp]
+    lib.gdn_resume.restype = ctypes.c_int
+    lib.gdn_prefill_emit_checkpoints.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p,
+                                                 ctypes.c_int32, vp, vp, vp, vp]
+    lib.gdn_prefill_emit_checkpoints.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load().gdn_version().decode()
+
+
+def _i64(seq) -> Optional[np.ndarray]:
+    if seq is None:
+        return None
+    return np.ascontiguousarray(np.asarray(seq, dtype=np.int64).reshape(-1))
+
+
+def _p64(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def kernel_for(B: int, H: int, dk: int, dv: int, dtype: torch.dtype, flags: int = 0) -> str:
+    """Name of the kernel the library runs for this shape: "recurrent" or "chunked"."""
+    sh = _shape(B, H, dk, dv, _DTYPES[dtype], flags)
+    r = int(load().gdn_kernel_for(ctypes.byref(sh)))
+    if r < 0:
+        raise GDNError(2, f"no kernel for B={B} H={H} d_k={dk} d_v={dv} {dtype} flags={flags}")
+    return "chunked" if r == 1 else "recurrent"
+
+
+def tail_len(m: int, r_num: int, r_den: int) -> int:
+    """k = ceil(r m), exact, capped at m; -1 for invalid arguments."""
+    return int(load().gdn_tail_len(int(m), int(r_num), int(r_den)))
+
+
+def select_checkpoint(positions: Sequence[int], depth: int) -> int:
+    """1-based index of the deepest checkpoint <= depth (0: none); -1 if invalid."""
+    pos = _i64(positions)
+    return int(load().gdn_select_checkpoint(_p64(pos), int(pos.size), int(depth)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensors(q, k, v, alpha, beta, o):
+    dt = k.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported element type {dt}; use float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dtype != dt:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dt}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    rows, H, dk = k.shape
+    dv = v.shape[2]
+    if v.shape[:2] != (rows, H) or alpha.shape != (rows, H) or beta.shape != (rows, H):
+        raise ValueError("v, alpha, beta must match k's [rows, H] layout")
+    if q is not None and q.shape != k.shape:
+        raise ValueError("q must have k's shape")
+    if o is not None and o.shape != v.shape:
+        raise ValueError("o must have v's shape")
+    return rows, H, dk, dv, _DTYPES[dt]
+
+
+def _shape(B, H, dk, dv, dtype, flags):
+    return _Shape(int(B), int(H), int(dk), int(dv), int(dtype), int(flags))
+
+
+def _state(t: Optional[torch.Tensor], shape, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be contiguous float32 of shape {tuple(shape)}")
+    return t
+
+
+def _check(status: int):
+    if status != 0:
+        raise GDNError(status, load().gdn_last_error().decode())
+
+
+def _rows_meta(tok_offset, first_pos, rows, B):
+    off = _i64(tok_offset)
+    if off.size != B + 1:
+        raise ValueError("tok_offset must have B + 1 entries")
+    if off[-1] > rows:
+        raise ValueError(f"tok_offset[-1] = {off[-1]} exceeds the {rows} stored rows")
+    fp = _i64(first_pos)
+    if fp is not None and fp.size != B:
+        raise ValueError("first_pos must have B entries")
+    return off, fp
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def tail_replay(q, k, v, alpha, beta, tok_offset, m, r_num, r_den, *, first_pos=None,
+                flags=NORMALIZE_K, state_out=None, o=None, want_o=True):
+    """Zero-start replay of the last ceil(r m_b) positions of each request.
+
+    Returns (state_out [B,H,d_v,d_k] float32, o or None, k_b list)."""
+    if want_o and o is None:
+        o = torch.empty_like(v)
+    rows, H, dk, dv, dt = _check_tensors(q if o is not None else None, k, v, alpha, beta, o)
+    mm = _i64(m)
+    B = int(mm.size)
+    off, fp = _rows_meta(tok_offset, first_pos, rows, B)
+    state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
+    kout = np.zeros(B, np.int64)
+    sh = _shape(B, H, dk, dv, dt, flags)
+    _check(load().gdn_tail_replay(ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k),
+                                  _ptr(v), _ptr(alpha), _ptr(beta), _p64(off), _p64(fp), _p64(mm),
+                                  int(r_num), int(r_den), _ptr(state_out), _ptr(o), _p64(kout),
+                                  _stream(k.device)))
+    return state_out, o, [int(x) for x in kout]
+
+
+def resume(q, k, v, alpha, beta, tok_offset, ckpt_pos, ckpt_states, depth, *, first_pos=None,
+           flags=NORMALIZE_K, state_out=None, o=None, want_o=True):
+    """Resume each request from its deepest checkpoint <= depth_b and recompute
+    up to depth_b.  ckpt_pos is [B][M]; ckpt_states [B, M, H, d_v, d_k] float32.
+
+    Returns (state_out, o or None, j_b list)."""
+    if want_o and o is None:
+        o = torch.empty_like(v)
+    rows, H, dk, dv, dt = _check_tensors(q if o is not None else None, k, v, alpha, beta, o)
+    dd = _i64(depth)
+    B = int(dd.size)
+    pos = np.ascontiguousarray(np.asarray(ckpt_pos, dtype=np.int64).reshape(B, -1))
+    M = int(pos.shape[1])
+    off, fp = _rows_meta(tok_offset, first_pos, rows, B)
+    if ckpt_states is not None:
+        if ckpt_states.dtype != torch.float32 or not ckpt_states.is_contiguous() or \
+                tuple(ckpt_states.shape) != (B, M, H, dv, dk):
+            raise ValueError(f"ckpt_states must be contiguous float32 [{B},{M},{H},{dv},{dk}]")
+    state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
+    jout = np.zeros(B, np.int32)
+    sh = _shape(B, H, dk, dv, dt, flags)
+    _check(load().gdn_resume(ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v),
+                             _ptr(alpha), _ptr(beta), _p64(off), _p64(fp),
+                             _p64(pos.reshape(-1)), M, _ptr(ckpt_states), _p64(dd),
+                             _ptr(state_out), _ptr(o),
+                             jout.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                             _stream(k.device)))
+    return state_out, o, [int(x) for x in jout]
+
+
+def prefill_emit_checkpoints(q, k, v, alpha, beta, tok_offset, ckpt_pos, *, flags=NORMALIZE_K,
+                             ckpt_states=None, state_out=None, o=None, want_o=True):
+    """Full prefill of every request from zero, storing the state after each
+    position in ckpt_pos[b] (strictly increasing, in [1, N_b]).
+
+    Returns (ckpt_states [B,M,H,d_v,d_k], state_out [B,H,d_v,d_k], o or None)."""
+    if want_o and o is None:
+        o = torch.empty_like(v)
+    rows, H, dk, dv, dt = _check_tensors(q if o is not None else None, k, v, alpha, beta, o)
+    off = _i64(tok_offset)
+    B = int(off.size) - 1
+    off, _ = _rows_meta(off, None, rows, B)
+    pos = np.ascontiguousarray(np.asarray(ckpt_pos, dtype=np.int64).reshape(B, -1))
+    M = int(pos.shape[1])
+    ckpt_states = _state(ckpt_states, (B, M, H, dv, dk), k.device, "ckpt_states")
+    state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
+    sh = _shape(B, H, dk, dv, dt, flags)
+    _check(load().gdn_prefill_emit_checkpoints(
+        ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
+        _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o), _stream(k.device)))
+    return ckpt_states, state_out, o

@@ -1,0 +1,369 @@
+// Host side of libgdnreplay: argument validation, exact integer span logic,
+// packing of the per-launch descriptors, and the exported C ABI declared in
+// include/gdnreplay.h.  No device memory is allocated and nothing is
+// synchronised; every launch is queued on the caller's stream.
+//
+// Span logic:
+//  - tail replay ("Tail-Replay: Escaping the Curse of Linear Attention in
+//    Prefix Caching for Hybrid LLMs" §2.1 symbol table and §2.2): k = ceil(r m)
+//    in exact integers, positions m - k + 1 .. m, zero start;
+//  - resume ("Sparse prefix caching for hybrid and recurrent LLM serving" §3):
+//    the deepest checkpoint c_j <= d (none: zero start), positions c_j + 1 .. d;
+//  - prefill with emission (same page, §3): positions 1 .. N from zero, the
+//    state after each checkpoint position is stored.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gdnreplay.h"
+#include "gdn_launch.h"
+
+#define GDN_API extern "C" __attribute__((visibility("default")))
+
+static_assert(gdn::kMaxEmitPerLaunch >= GDN_MAX_CHECKPOINTS,
+              "one request's emissions must fit one launch");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool valid_width(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+constexpr uint32_t kKnownFlags =
+    GDN_NORMALIZE_K | GDN_NORMALIZE_Q | GDN_KERNEL_RECURRENT | GDN_KERNEL_CHUNKED;
+
+// One request's work: scan `len` tokens starting at packed row `row0`, from
+// the state at `init_off` (-1: zero), emitting at span-relative counts.
+struct Work {
+    int32_t b;
+    int64_t row0;
+    int64_t len;
+    int64_t init_off;
+    std::vector<std::pair<int32_t, int32_t>> emits;  // (count after, slot)
+};
+
+gdn_status check_shape(const gdn_shape *s) {
+    if (!s) return fail(GDN_ERR_INVALID_ARGUMENT, "shape is NULL");
+    if (s->B < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "B = %d < 0", s->B);
+    if (s->H < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "H = %d < 1", s->H);
+    if (!valid_width(s->dk) || !valid_width(s->dv))
+        return fail(GDN_ERR_UNSUPPORTED, "d_k = %d, d_v = %d: each must be 16, 32, 64 or 128",
+                    s->dk, s->dv);
+    if (s->dtype != GDN_DTYPE_F32 && s->dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "unknown dtype %d", s->dtype);
+    if (s->flags & ~kKnownFlags)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", s->flags & ~kKnownFlags);
+    if ((s->flags & GDN_KERNEL_RECURRENT) && (s->flags & GDN_KERNEL_CHUNKED))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_KERNEL_RECURRENT and GDN_KERNEL_CHUNKED both set");
+    return GDN_OK;
+}
+
+gdn_status check_rows(const gdn_shape *s, const int64_t *off, const int64_t *first) {
+    if (!off) return fail(GDN_ERR_INVALID_ARGUMENT, "h_tok_offset is NULL");
+    if (off[0] < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "h_tok_offset[0] = %lld < 0", (long long)off[0]);
+    for (int32_t b = 0; b < s->B; ++b) {
+        if (off[b + 1] < off[b])
+            return fail(GDN_ERR_INVALID_ARGUMENT, "h_tok_offset decreases at request %d", b);
+        if (first && first[b] < 1)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "h_first_pos[%d] = %lld < 1", b, (long long)first[b]);
+    }
+    const int64_t rows = off[s->B];
+    const int64_t wmax = s->dk > s->dv ? s->dk : s->dv;
+    if (rows > (INT64_MAX / 4) / ((int64_t)s->H * wmax))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "too many rows (%lld)", (long long)rows);
+    return GDN_OK;
+}
+
+// The span [p0, p0 + len) must lie inside the stored rows of request b.
+gdn_status span_to_rows(int32_t b, const int64_t *off, const int64_t *first, int64_t p0,
+                        int64_t len, int64_t *row0) {
+    const int64_t f = first ? first[b] : 1;
+    const int64_t n = off[b + 1] - off[b];
+    *row0 = off[b] + (p0 - f);
+    if (len == 0) {
+        *row0 = off[b];
+        return GDN_OK;
+    }
+    if (p0 < f || p0 + len - 1 > f + n - 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT,
+                    "request %d: span positions %lld..%lld are not stored (rows hold %lld..%lld)",
+                    b, (long long)p0, (long long)(p0 + len - 1), (long long)f, (long long)(f + n - 1));
+    if (len > INT32_MAX)
+        return fail(GDN_ERR_UNSUPPORTED, "request %d: span of %lld tokens exceeds 2^31 - 1", b,
+                    (long long)len);
+    return GDN_OK;
+}
+
+gdn_status check_positions(const int64_t *pos, int32_t B, int32_t M) {
+    if (M < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "M = %d < 0", M);
+    if (M > GDN_MAX_CHECKPOINTS)
+        return fail(GDN_ERR_UNSUPPORTED, "M = %d exceeds %d checkpoints per request", M,
+                    GDN_MAX_CHECKPOINTS);
+    if (M > 0 && B > 0 && !pos) return fail(GDN_ERR_INVALID_ARGUMENT, "h_ckpt_pos is NULL");
+    for (int32_t b = 0; b < B; ++b)
+        for (int32_t i = 0; i < M; ++i) {
+            const int64_t c = pos[(int64_t)b * M + i];
+            if (c < 1)
+                return fail(GDN_ERR_INVALID_ARGUMENT, "request %d: checkpoint %d at %lld < 1", b, i,
+                            (long long)c);
+            if (i > 0 && c <= pos[(int64_t)b * M + i - 1])
+                return fail(GDN_ERR_INVALID_ARGUMENT,
+                            "request %d: checkpoint positions not strictly increasing at %d", b, i);
+        }
+    return GDN_OK;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const char *pa = static_cast<const char *>(a);
+    const char *pb = static_cast<const char *>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// Validate pointers, pick the kernel and queue the launches.
+gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
+               const void *alpha, const void *beta, void *o, float *state_out,
+               const float *init_base, float *emit_base, int32_t M,
+               const std::vector<Work> &work, hipStream_t stream) {
+    bool any_tokens = false;
+    for (const Work &w : work) any_tokens |= w.len > 0;
+    if (!state_out && !work.empty()) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is NULL");
+    if (any_tokens) {
+        if (!k || !v || !alpha || !beta)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "k, v, alpha and beta must be non-NULL");
+        if (o && !q) return fail(GDN_ERR_INVALID_ARGUMENT, "o is set but q is NULL");
+    }
+    const gdn::Elem elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
+    bool chunked = gdn::chunked_supported(s->dk, s->dv, elem) && !(s->flags & GDN_KERNEL_RECURRENT);
+    if ((s->flags & GDN_KERNEL_CHUNKED) && !gdn::chunked_supported(s->dk, s->dv, elem))
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "GDN_KERNEL_CHUNKED: no chunked kernel for d_k = %d, d_v = %d, dtype %d",
+                    s->dk, s->dv, s->dtype);
+
+    gdn::LaunchDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.q = q;
+    d.k = k;
+    d.v = v;
+    d.alpha = alpha;
+    d.beta = beta;
+    d.o = o;
+    d.state_out = state_out;
+    d.init_base = init_base;
+    d.emit_base = emit_base;
+    d.H = s->H;
+    d.flags = (int32_t)(s->flags & (GDN_NORMALIZE_K | GDN_NORMALIZE_Q));
+    d.M = M;
+
+    size_t i = 0;
+    while (i < work.size()) {
+        int nreq = 0, nemit = 0;
+        d.emit_begin[0] = 0;
+        while (i < work.size() && nreq < gdn::kMaxReqPerLaunch &&
+               nemit + (int)work[i].emits.size() <= gdn::kMaxEmitPerLaunch) {
+            const Work &w = work[i];
+            d.row0[nreq] = w.row0;
+            d.init_off[nreq] = w.init_off;
+            d.len[nreq] = (int32_t)w.len;
+            d.req[nreq] = w.b;
+            for (const auto &e : w.emits) {
+                d.emit_after[nemit] = e.first;
+                d.emit_slot[nemit] = e.second;
+                ++nemit;
+            }
+            d.emit_begin[nreq + 1] = nemit;
+            ++nreq;
+            ++i;
+        }
+        if (nreq == 0)  // cannot happen: one request never exceeds the emission budget
+            return fail(GDN_ERR_UNSUPPORTED, "emission list does not fit one launch");
+        d.nreq = nreq;
+        hipError_t err = chunked ? gdn::launch_chunked(d, s->dk, s->dv, elem, stream)
+                                 : gdn::launch_recurrent(d, s->dk, s->dv, elem, stream);
+        if (err != hipSuccess)
+            return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    }
+    return GDN_OK;
+}
+
+int64_t tail_len_exact(int64_t m, int64_t r_num, int64_t r_den) {
+    if (m < 0 || r_num < 0 || r_den <= 0) return -1;
+    const __int128 num = (__int128)m * r_num;
+    __int128 k = (num + r_den - 1) / r_den;  // ceiling of a non-negative ratio
+    if (k > m) k = m;
+    return (int64_t)k;
+}
+
+int32_t select_exact(const int64_t *pos, int32_t M, int64_t depth) {
+    int32_t j = 0;
+    for (int32_t i = 0; i < M; ++i)
+        if (pos[i] <= depth) j = i + 1;
+    return j;
+}
+
+}  // namespace
+
+GDN_API const char *gdn_version(void) { return "libgdnreplay 0.1.0 gfx950"; }
+
+GDN_API const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+GDN_API int32_t gdn_kernel_for(const gdn_shape *shape) {
+    if (check_shape(shape) != GDN_OK) return -1;
+    const gdn::Elem elem = shape->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
+    const bool has_chunked = gdn::chunked_supported(shape->dk, shape->dv, elem);
+    if ((shape->flags & GDN_KERNEL_CHUNKED) && !has_chunked) return -1;
+    return (has_chunked && !(shape->flags & GDN_KERNEL_RECURRENT)) ? 1 : 0;
+}
+
+GDN_API int64_t gdn_tail_len(int64_t m, int64_t r_num, int64_t r_den) {
+    return tail_len_exact(m, r_num, r_den);
+}
+
+GDN_API int32_t gdn_select_checkpoint(const int64_t *pos, int32_t M, int64_t depth) {
+    if (M < 0 || depth < 0 || (M > 0 && !pos)) return -1;
+    for (int32_t i = 0; i < M; ++i)
+        if (pos[i] < 1 || (i > 0 && pos[i] <= pos[i - 1])) return -1;
+    return select_exact(pos, M, depth);
+}
+
+GDN_API gdn_status gdn_tail_replay(const gdn_shape *shape, const void *q, const void *k,
+                                   const void *v, const void *alpha, const void *beta,
+                                   const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                                   const int64_t *h_m, int64_t r_num, int64_t r_den,
+                                   float *state_out, void *o, int64_t *h_k_out,
+                                   hipStream_t stream) {
+    g_last_error.clear();
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    if (shape->B == 0) return GDN_OK;
+    if ((st = check_rows(shape, h_tok_offset, h_first_pos)) != GDN_OK) return st;
+    if (!h_m) return fail(GDN_ERR_INVALID_ARGUMENT, "h_m is NULL");
+    if (r_num < 0 || r_den <= 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "replay ratio %lld/%lld invalid", (long long)r_num,
+                    (long long)r_den);
+    std::vector<Work> work(shape->B);
+    std::vector<int64_t> ks(shape->B);
+    for (int32_t b = 0; b < shape->B; ++b) {
+        if (h_m[b] < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "h_m[%d] < 0", b);
+        const int64_t kb = tail_len_exact(h_m[b], r_num, r_den);
+        ks[b] = kb;
+        Work &w = work[b];
+        w.b = b;
+        w.len = kb;
+        w.init_off = -1;
+        if ((st = span_to_rows(b, h_tok_offset, h_first_pos, h_m[b] - kb + 1, kb, &w.row0)) != GDN_OK)
+            return st;
+    }
+    st = run(shape, q, k, v, alpha, beta, o, state_out, nullptr, nullptr, 0, work, stream);
+    if (st == GDN_OK && h_k_out)
+        for (int32_t b = 0; b < shape->B; ++b) h_k_out[b] = ks[b];
+    return st;
+}
+
+GDN_API gdn_status gdn_resume(const gdn_shape *shape, const void *q, const void *k,
+                              const void *v, const void *alpha, const void *beta,
+                              const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                              const int64_t *h_ckpt_pos, int32_t M, const float *ckpt_states,
+                              const int64_t *h_depth, float *state_out, void *o,
+                              int32_t *h_j_out, hipStream_t stream) {
+    g_last_error.clear();
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    if (shape->B == 0) return GDN_OK;
+    if ((st = check_rows(shape, h_tok_offset, h_first_pos)) != GDN_OK) return st;
+    if ((st = check_positions(h_ckpt_pos, shape->B, M)) != GDN_OK) return st;
+    if (!h_depth) return fail(GDN_ERR_INVALID_ARGUMENT, "h_depth is NULL");
+    if (!state_out) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is NULL");
+    const int64_t slot = (int64_t)shape->H * shape->dv * shape->dk;  // floats per (b, slot)
+    std::vector<Work> work(shape->B);
+    std::vector<int32_t> js(shape->B);
+    for (int32_t b = 0; b < shape->B; ++b) {
+        const int64_t dpt = h_depth[b];
+        if (dpt < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "h_depth[%d] < 0", b);
+        const int32_t j = select_exact(h_ckpt_pos + (int64_t)b * M, M, dpt);
+        js[b] = j;
+        const int64_t c = j > 0 ? h_ckpt_pos[(int64_t)b * M + j - 1] : 0;
+        Work &w = work[b];
+        w.b = b;
+        w.len = dpt - c;
+        w.init_off = j > 0 ? ((int64_t)b * M + (j - 1)) * slot : -1;
+        if (j > 0 && !ckpt_states)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "request %d selects checkpoint %d but ckpt_states is NULL", b, j);
+        if ((st = span_to_rows(b, h_tok_offset, h_first_pos, c + 1, w.len, &w.row0)) != GDN_OK)
+            return st;
+    }
+    // state_out may coincide with a request's own selected slot; any other
+    // overlap with a slot that is read would race.
+    if (ckpt_states) {
+        const size_t sb = (size_t)slot * sizeof(float);
+        for (int32_t b = 0; b < shape->B; ++b) {
+            const float *out_b = state_out + (int64_t)b * slot;
+            for (int32_t b2 = 0; b2 < shape->B; ++b2) {
+                if (work[b2].init_off < 0) continue;
+                const float *in_b2 = ckpt_states + work[b2].init_off;
+                if (ranges_overlap(out_b, sb, in_b2, sb) && !(b == b2 && out_b == in_b2))
+                    return fail(GDN_ERR_INVALID_ARGUMENT,
+                                "state_out of request %d overlaps the checkpoint read by request %d", b, b2);
+            }
+        }
+    }
+    st = run(shape, q, k, v, alpha, beta, o, state_out, ckpt_states, nullptr, M, work, stream);
+    if (st == GDN_OK && h_j_out)
+        for (int32_t b = 0; b < shape->B; ++b) h_j_out[b] = js[b];
+    return st;
+}
+
+GDN_API gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape, const void *q,
+                                                const void *k, const void *v,
+                                                const void *alpha, const void *beta,
+                                                const int64_t *h_tok_offset,
+                                                const int64_t *h_first_pos,
+                                                const int64_t *h_ckpt_pos, int32_t M,
+                                                float *ckpt_states, float *state_out, void *o,
+                                                hipStream_t stream) {
+    g_last_error.clear();
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    if (shape->B == 0) return GDN_OK;
+    if ((st = check_rows(shape, h_tok_offset, h_first_pos)) != GDN_OK) return st;
+    if ((st = check_positions(h_ckpt_pos, shape->B, M)) != GDN_OK) return st;
+    if (M > 0 && !ckpt_states) return fail(GDN_ERR_INVALID_ARGUMENT, "ckpt_states is NULL");
+    if (!state_out) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is NULL");
+    const int64_t slot = (int64_t)shape->H * shape->dv * shape->dk;
+    if (M > 0 && ranges_overlap(state_out, (size_t)shape->B * slot * sizeof(float), ckpt_states,
+                                (size_t)shape->B * M * slot * sizeof(float)))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "state_out overlaps ckpt_states");
+    std::vector<Work> work(shape->B);
+    for (int32_t b = 0; b < shape->B; ++b) {
+        if (h_first_pos && h_first_pos[b] != 1)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "prefill needs the whole prefix: h_first_pos[%d] = %lld",
+                        b, (long long)h_first_pos[b]);
+        const int64_t n = h_tok_offset[b + 1] - h_tok_offset[b];
+        Work &w = work[b];
+        w.b = b;
+        w.len = n;
+        w.init_off = -1;
+        if ((st = span_to_rows(b, h_tok_offset, nullptr, 1, n, &w.row0)) != GDN_OK) return st;
+        for (int32_t i = 0; i < M; ++i) {
+            const int64_t c = h_ckpt_pos[(int64_t)b * M + i];
+            if (c > n)
+                return fail(GDN_ERR_INVALID_ARGUMENT, "request %d: checkpoint %lld beyond N = %lld", b,
+                            (long long)c, (long long)n);
+            w.emits.emplace_back((int32_t)c, i);
+        }
+    }
+    return run(shape, q, k, v, alpha, beta, o, state_out, nullptr, ckpt_states, M, work, stream);
+}

@@ -1,0 +1,181 @@
+/*
+ * gdnreplay.h - C ABI of libgdnreplay: Gated DeltaNet span replay on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [TR]  "Tail-Replay: Escaping the Curse of Linear Attention in Prefix
+ *         Caching for Hybrid LLMs" (notes page on arXiv 2608.30310v2).
+ *   [SPC] "Sparse prefix caching for hybrid and recurrent LLM serving"
+ *         (arXiv 2605.05219).
+ *
+ * The operation ([TR] §2.3, eq. (1)).  Per (request, head) a state S of
+ * d_v x d_k float32 values (row-major, d_k contiguous) is carried through the
+ * tokens of a span.  The key operator acts from the right, which is the only
+ * reading that type-checks for a rectangular state ([TR] §2.3):
+ *     S_i = alpha_i S_{i-1} (I - beta_i k_i k_i^T) + beta_i v_i k_i^T
+ *         = alpha_i S_{i-1} + beta_i (v_i - alpha_i S_{i-1} k_i) k_i^T,
+ * and every token of the span produces o_i = S_i q_i from the updated state.
+ * With GDN_NORMALIZE_K (GDN_NORMALIZE_Q) each key (query) is first divided by
+ * its L2 norm, computed in float32; a zero vector stays zero.
+ *
+ * Packed token layout, shared by every call (element types per gdn_dtype):
+ *   q, k   [rows][H][d_k]      v, o   [rows][H][d_v]      alpha, beta  [rows][H]
+ * Request b owns rows tok_offset[b] .. tok_offset[b+1]-1; row tok_offset[b]
+ * holds the token at 1-based position first_pos[b] of that request
+ * (first_pos == NULL means 1 for every request), so a caller may store a whole
+ * prefix or only the rows a span needs.  A "position" c counts tokens: the
+ * state "at c" is the state after the c-th token.
+ * States: state_out [B][H][d_v][d_k] float32; checkpoint stores
+ * [B][M][H][d_v][d_k] float32.
+ *
+ * Conventions for all entry points:
+ *  - Device pointers (q, k, v, alpha, beta, o, state_out, ckpt_states) must
+ *    be device memory of the current HIP device; arguments prefixed h_ are
+ *    host arrays, read during the call only.  The caller owns every buffer.
+ *    The library allocates nothing, keeps no device state beyond its code
+ *    object and never synchronises: work is queued on `stream` (NULL = the
+ *    null stream) and results are ready when that stream has drained.
+ *  - Only the rows of a span are read from q, k, v, alpha, beta; o is written
+ *    on the rows of the span only (other rows are left untouched); o == NULL
+ *    skips the outputs (q may then be NULL).
+ *  - Thread-safe: calls keep no shared mutable state (the error text is
+ *    thread-local).
+ *  - Errors: GDN_ERR_INVALID_ARGUMENT / GDN_ERR_UNSUPPORTED are detected on the
+ *    host before anything is queued; GDN_ERR_HIP reports a failed launch.  In
+ *    every error case gdn_last_error() describes it.  A fault inside a kernel
+ *    surfaces at the caller's synchronisation of `stream`.
+ */
+#ifndef GDNREPLAY_H
+#define GDNREPLAY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1,
+    GDN_ERR_UNSUPPORTED = 2,
+    GDN_ERR_HIP = 3
+} gdn_status;
+
+/* Element type of q, k, v, alpha, beta and o.  States are always float32. */
+typedef enum gdn_dtype { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+
+/* gdn_shape.flags */
+#define GDN_NORMALIZE_K 1u        /* divide each key by its L2 norm before use   */
+#define GDN_NORMALIZE_Q 2u        /* divide each query by its L2 norm before use */
+#define GDN_KERNEL_RECURRENT 256u /* force the per-token float32 kernel          */
+#define GDN_KERNEL_CHUNKED 512u   /* require the chunked matrix-core kernel      */
+
+/* Largest number of checkpoint positions per request (emission and resume). */
+#define GDN_MAX_CHECKPOINTS 192
+
+typedef struct gdn_shape {
+    int32_t B;      /* requests, >= 0                                  */
+    int32_t H;      /* heads, >= 1                                     */
+    int32_t dk;     /* key width: 16, 32, 64 or 128                    */
+    int32_t dv;     /* value width: 16, 32, 64 or 128                  */
+    int32_t dtype;  /* gdn_dtype                                       */
+    uint32_t flags; /* GDN_NORMALIZE_K | GDN_NORMALIZE_Q | GDN_KERNEL_* */
+} gdn_shape;
+
+/* Library version string, e.g. "libgdnreplay 0.1.0 gfx950". */
+const char *gdn_version(void);
+
+/* Text of the last error reported on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/*
+ * Which kernel the entry points would run for this shape: 0 = the per-token
+ * float32 kernel, 1 = the chunked matrix-core kernel, -1 = the shape (or a
+ * GDN_KERNEL_* request in its flags) is not supported.  Host only.
+ */
+int32_t gdn_kernel_for(const gdn_shape *shape);
+
+/*
+ * Tail length k = ceil(r m) with r = r_num / r_den, in exact integer
+ * arithmetic, capped at m ([TR] §2.1 symbol table; §2.2: m = 10000 and r = 5%
+ * replay positions 9501..10000).  Returns -1 if m < 0, r_num < 0 or r_den <= 0.
+ * Host only.
+ */
+int64_t gdn_tail_len(int64_t m, int64_t r_num, int64_t r_den);
+
+/*
+ * Deepest checkpoint at or before depth ([SPC] §3): returns the 1-based index
+ * j of the largest pos[j-1] <= depth, or 0 when none qualifies (recompute from
+ * the zero state, the implicit c_0 = 0).  pos must hold M strictly increasing
+ * positions >= 1.  Returns -1 if pos is NULL with M > 0, M < 0, depth < 0 or
+ * pos is not strictly increasing.  Host only.
+ */
+int32_t gdn_select_checkpoint(const int64_t *pos, int32_t M, int64_t depth);
+
+/*
+ * Zero-start tail replay ([TR] §2.2): for each request b, k_b = ceil(r m_b)
+ * and the state is rebuilt from zero over positions m_b - k_b + 1 .. m_b.
+ *   h_m        host [B], m_b >= 0 (m_b = 0 gives k_b = 0 and a zero state)
+ *   r_num/r_den  replay ratio r, r_num >= 0, r_den > 0
+ *   state_out  device [B][H][d_v][d_k] float32: the replayed state at m_b
+ *   o          device, nullable: outputs on the replayed rows
+ *   h_k_out    host [B], nullable: receives k_b
+ * The rows of positions m_b - k_b + 1 .. m_b must be stored.
+ */
+gdn_status gdn_tail_replay(const gdn_shape *shape,
+                           const void *q, const void *k, const void *v,
+                           const void *alpha, const void *beta,
+                           const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                           const int64_t *h_m, int64_t r_num, int64_t r_den,
+                           float *state_out, void *o, int64_t *h_k_out,
+                           hipStream_t stream);
+
+/*
+ * Resume from a sparse checkpoint ([SPC] §3): for each request b,
+ * j_b = gdn_select_checkpoint(h_ckpt_pos + b*M, M, h_depth[b]); the scan
+ * starts from ckpt_states[b][j_b - 1] (or from zero when j_b = 0) and
+ * recomputes positions c_{j_b} + 1 .. depth_b.  A depth equal to a checkpoint
+ * copies that state bit-for-bit; depth 0 gives the zero state.
+ *   h_ckpt_pos   host [B][M], strictly increasing per request, >= 1
+ *   ckpt_states  device [B][M][H][d_v][d_k] float32 (read only); may be NULL
+ *                if no request selects a checkpoint
+ *   h_depth      host [B], >= 0
+ *   state_out    device [B][H][d_v][d_k]: the state at depth_b.  It may alias
+ *                the selected slot ckpt_states[b][j_b - 1] exactly.
+ *   h_j_out      host [B], nullable: receives j_b
+ * The rows of positions c_{j_b} + 1 .. depth_b must be stored.
+ */
+gdn_status gdn_resume(const gdn_shape *shape,
+                      const void *q, const void *k, const void *v,
+                      const void *alpha, const void *beta,
+                      const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                      const int64_t *h_ckpt_pos, int32_t M, const float *ckpt_states,
+                      const int64_t *h_depth, float *state_out, void *o,
+                      int32_t *h_j_out, hipStream_t stream);
+
+/*
+ * Full prefill with checkpoint emission ([SPC] §3: a state is kept at every
+ * checkpoint position): for each request b the scan runs from the zero state over all its
+ * N_b = tok_offset[b+1] - tok_offset[b] rows (first_pos must be NULL or 1) and
+ * writes the state after position h_ckpt_pos[b][i] to ckpt_states[b][i].
+ *   h_ckpt_pos   host [B][M], strictly increasing per request, in [1, N_b]
+ *   ckpt_states  device [B][M][H][d_v][d_k] float32 (written); may be NULL if M = 0
+ *   state_out    device [B][H][d_v][d_k]: the state at N_b
+ */
+gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape,
+                                        const void *q, const void *k, const void *v,
+                                        const void *alpha, const void *beta,
+                                        const int64_t *h_tok_offset,
+                                        const int64_t *h_first_pos,
+                                        const int64_t *h_ckpt_pos, int32_t M,
+                                        float *ckpt_states, float *state_out, void *o,
+                                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDNREPLAY_H */

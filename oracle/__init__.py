@@ -24,7 +24,7 @@ What is computed (all arithmetic in float64):
   * span selection: resume from the deepest checkpoint c_j <= d ([SPC] §3),
     zero-start tail replay of the last k = ceil(r*m) positions ([TR] §2.1
     symbol table and §2.2), full prefill 1..N with states emitted at the
-    checkpoint positions ([SPC] §3, "the state at c_i is stored").
+    checkpoint positions ([SPC] §3: a state is kept at every checkpoint).
 
 Two forms of the scan are provided:
   ``scan_literal``  builds the d_k x d_k transition T_i = alpha_i (I - beta_i k k^T)

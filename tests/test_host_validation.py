@@ -1,0 +1,135 @@
+"""Host-side argument validation of the C ABI.
+
+Each call passes placeholder device addresses that validation must reject
+before any HIP API is touched.  The module runs only where no GPU is visible,
+so that a validation bug can never become a launch on real memory.
+"""
+import ctypes
+import os
+
+import pytest
+import torch
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_delta_rule_scan_amd as g
+    if not os.path.exists(g.library_path()):
+        from gated_delta_rule_scan_amd.build import build
+        build()
+    return g
+
+
+# --- argument validation (host only: each call fails before any launch) ------
+# These calls pass placeholder device addresses that validation must reject.
+# They run only where no GPU is visible, so that a validation bug can never
+# turn into a launch on real memory.
+
+FAKE = 0x1000  # never dereferenced: validation rejects the call first
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="placeholder-pointer validation runs only without a GPU")
+
+
+def _call_tail(gdn, shape_kw=None, **kw):
+    lib = gdn.load()
+    sk = dict(B=2, H=2, dk=128, dv=128, dtype=1, flags=1)
+    sk.update(shape_kw or {})
+    sh = gdn._Shape(**sk)
+    a = dict(off=[0, 10, 20], first=None, m=[10, 10], r_num=5, r_den=100,
+             state=FAKE, o=FAKE)
+    a.update(kw)
+    off = gdn._i64(a["off"])
+    first = gdn._i64(a["first"])
+    m = gdn._i64(a["m"])
+    p = ctypes.c_void_p(FAKE)
+    st = lib.gdn_tail_replay(ctypes.byref(sh), p, p, p, p, p, gdn._p64(off), gdn._p64(first),
+                             gdn._p64(m), a["r_num"], a["r_den"],
+                             ctypes.c_void_p(a["state"]) if a["state"] else None,
+                             ctypes.c_void_p(a["o"]) if a["o"] else None, None, None)
+    return st, lib.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("shape_kw,code", [
+    ({"dk": 96}, 2), ({"dv": 8}, 2), ({"dtype": 7}, 1), ({"H": 0}, 1), ({"B": -1}, 1),
+    ({"flags": 1 << 20}, 1), ({"flags": 256 | 512}, 1),
+])
+def test_shape_errors(gdn, shape_kw, code):
+    st, msg = _call_tail(gdn, shape_kw)
+    assert st == code and msg
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(off=[0, 10, 5]), "decreases"),
+    (dict(off=[-1, 10, 20]), "< 0"),
+    (dict(first=[0, 1]), "h_first_pos"),
+    (dict(m=[11, 10]), "not stored"),
+    (dict(m=[-3, 10]), "h_m"),
+    (dict(r_den=0), "ratio"),
+    (dict(r_num=-1), "ratio"),
+    (dict(state=0), "state_out"),
+])
+def test_tail_argument_errors(gdn, kw, needle):
+    st, msg = _call_tail(gdn, **kw)
+    assert st == 1 and needle in msg, msg
+
+
+def test_tail_span_outside_stored_tail_rows(gdn):
+    # rows hold positions 91..100 of each request; m = 100, r = 20% needs 81..100
+    st, msg = _call_tail(gdn, first=[91, 91], m=[100, 100], r_num=20, r_den=100)
+    assert st == 1 and "not stored" in msg
+
+
+def test_chunked_required_but_unavailable_for_f32(gdn):
+    st, msg = _call_tail(gdn, {"dtype": 0, "flags": 512})
+    assert st == 2 and "CHUNKED" in msg
+
+
+def _call_resume(gdn, pos, depth, states=FAKE, out=FAKE, M=None, off=(0, 50)):
+    lib = gdn.load()
+    B = len(depth)
+    sh = gdn._Shape(B, 1, 16, 16, 0, 1)
+    offa = gdn._i64(off)
+    posa = gdn._i64(pos)
+    M = len(pos) // B if M is None else M
+    p = ctypes.c_void_p(FAKE)
+    st = lib.gdn_resume(ctypes.byref(sh), p, p, p, p, p, gdn._p64(offa), None, gdn._p64(posa), M,
+                        ctypes.c_void_p(states) if states else None, gdn._p64(gdn._i64(depth)),
+                        ctypes.c_void_p(out) if out else None, None, None, None)
+    return st, lib.gdn_last_error().decode()
+
+
+def test_resume_errors(gdn):
+    assert _call_resume(gdn, [5, 5], [7])[0] == 1          # not strictly increasing
+    assert _call_resume(gdn, [0, 5], [7])[0] == 1          # position < 1
+    assert _call_resume(gdn, [5, 9], [-1])[0] == 1         # negative depth
+    assert _call_resume(gdn, [5, 9], [60])[0] == 1         # span beyond stored rows
+    assert _call_resume(gdn, [5, 9], [7], states=0)[0] == 1  # selects a slot, no store
+    st, msg = _call_resume(gdn, [5] * 1, [7], M=300)
+    assert st == 2 and "exceeds" in msg
+    # state_out overlapping another request's selected slot is rejected
+    base = 0x100000
+    slot = 16 * 16 * 4
+    # request 1 reads slot (1, 1) = bytes [3 slot, 4 slot); request 0 writes there
+    st, msg = _call_resume(gdn, [5, 9, 5, 9], [7, 9], states=base, out=base + 3 * slot,
+                           off=(0, 50, 100))
+    assert st == 1 and "overlaps" in msg
+
+
+def test_prefill_errors(gdn):
+    lib = gdn.load()
+    sh = gdn._Shape(1, 1, 16, 16, 0, 1)
+    p = ctypes.c_void_p(FAKE)
+    off = gdn._i64([0, 20])
+
+    def call(pos, first=None, states=FAKE, out=FAKE + 10 ** 9):
+        posa = gdn._i64(pos)
+        return lib.gdn_prefill_emit_checkpoints(
+            ctypes.byref(sh), p, p, p, p, p, gdn._p64(off), gdn._p64(gdn._i64(first)),
+            gdn._p64(posa), len(pos), ctypes.c_void_p(states) if states else None,
+            ctypes.c_void_p(out), None, None)
+
+    assert call([5, 21]) == 1                  # beyond N
+    assert call([5, 4]) == 1                   # not increasing
+    assert call([5], first=[2]) == 1           # prefill needs position 1
+    assert call([5], states=0) == 1            # emission store missing
+    assert call([5], out=FAKE) == 1            # state_out overlaps the store
