@@ -133,6 +133,16 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
+// 0: per-token kernel, 1: chunked kernel, -1: GDN_KERNEL_CHUNKED cannot be honoured.
+// The chunked kernel needs unit keys: its fp16 operand ranges rely on them.
+int32_t kernel_choice(const gdn_shape *s) {
+    const gdn::Elem elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
+    const bool has_chunked =
+        gdn::chunked_supported(s->dk, s->dv, elem) && (s->flags & GDN_NORMALIZE_K);
+    if ((s->flags & GDN_KERNEL_CHUNKED) && !has_chunked) return -1;
+    return (has_chunked && !(s->flags & GDN_KERNEL_RECURRENT)) ? 1 : 0;
+}
+
 // Validate pointers, pick the kernel and queue the launches.
 gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
                const void *alpha, const void *beta, void *o, float *state_out,
@@ -146,12 +156,14 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
             return fail(GDN_ERR_INVALID_ARGUMENT, "k, v, alpha and beta must be non-NULL");
         if (o && !q) return fail(GDN_ERR_INVALID_ARGUMENT, "o is set but q is NULL");
     }
-    const gdn::Elem elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
-    bool chunked = gdn::chunked_supported(s->dk, s->dv, elem) && !(s->flags & GDN_KERNEL_RECURRENT);
-    if ((s->flags & GDN_KERNEL_CHUNKED) && !gdn::chunked_supported(s->dk, s->dv, elem))
+    const int32_t kern = kernel_choice(s);
+    if (kern < 0)
         return fail(GDN_ERR_UNSUPPORTED,
-                    "GDN_KERNEL_CHUNKED: no chunked kernel for d_k = %d, d_v = %d, dtype %d",
-                    s->dk, s->dv, s->dtype);
+                    "GDN_KERNEL_CHUNKED: no chunked kernel for d_k = %d, d_v = %d, dtype %d, flags 0x%x "
+                    "(it needs bf16, d_k = d_v = 128 and GDN_NORMALIZE_K)",
+                    s->dk, s->dv, s->dtype, s->flags);
+    const gdn::Elem elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
+    const bool chunked = kern == 1;
 
     gdn::LaunchDesc d;
     std::memset(&d, 0, sizeof(d));
@@ -222,10 +234,7 @@ GDN_API const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
 GDN_API int32_t gdn_kernel_for(const gdn_shape *shape) {
     if (check_shape(shape) != GDN_OK) return -1;
-    const gdn::Elem elem = shape->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
-    const bool has_chunked = gdn::chunked_supported(shape->dk, shape->dv, elem);
-    if ((shape->flags & GDN_KERNEL_CHUNKED) && !has_chunked) return -1;
-    return (has_chunked && !(shape->flags & GDN_KERNEL_RECURRENT)) ? 1 : 0;
+    return kernel_choice(shape);
 }
 
 GDN_API int64_t gdn_tail_len(int64_t m, int64_t r_num, int64_t r_den) {

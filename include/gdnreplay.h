@@ -71,7 +71,7 @@ typedef enum gdn_dtype { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
 #define GDN_NORMALIZE_K 1u        /* divide each key by its L2 norm before use   */
 #define GDN_NORMALIZE_Q 2u        /* divide each query by its L2 norm before use */
 #define GDN_KERNEL_RECURRENT 256u /* force the per-token float32 kernel          */
-#define GDN_KERNEL_CHUNKED 512u   /* require the chunked matrix-core kernel      */
+#define GDN_KERNEL_CHUNKED 512u   /* require the chunked matrix-core kernel (bf16, d_k = d_v = 128, GDN_NORMALIZE_K) */
 
 /* Largest number of checkpoint positions per request (emission and resume). */
 #define GDN_MAX_CHECKPOINTS 192
