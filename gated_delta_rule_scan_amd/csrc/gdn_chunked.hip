@@ -17,12 +17,15 @@
 // This is the compact-WY way of applying a product of rank-1 modifications of
 // the identity (Golub & Van Loan, Matrix Computations, §5.1) to the chunk.
 //
-// Precision: the dense products run on fp16 MFMA (v_mfma_f32_32x32x16_f16 and
-// v_mfma_f32_16x16x32_f16) with float32 accumulation.  Every fp16 operand is
-// range-scaled by an exact power of two: keys/queries per token (k' = k/2^E
-// with max|k'| < 1, exact for bf16 data), the state, B, U and T per wave or
-// per chunk.  The triangular inverse T is formed in float32 on VALU.  The
-// state itself never leaves float32.
+// Precision: the dense products run on fp16 MFMA (32x32x16, 16x16x32 and
+// 16x16x16 shapes) with float32 accumulation.  Keys are unit vectors (the
+// fused L2 norm), so |k_i| <= 1 fits fp16 as is; queries are normalised too,
+// or scaled per token by an exact power of two.  The state, B, U and T are
+// scaled by exact powers of two per wave or per chunk before rounding to
+// fp16.  T is built blockwise: 16x16 diagonal blocks by float32 substitution,
+// the off-diagonal blocks by two doubling levels on MFMA.  The state itself
+// never leaves float32.  Gates are handled in log2 space with the native
+// v_exp_f32 / v_log_f32.
 //
 // Work split: one workgroup of 4 waves per (request, head); wave w owns value
 // rows [32w, 32w + 32).  The state is kept transposed, S^T (d_k x d_v), in
@@ -51,24 +54,31 @@ constexpr int TST = C + 4;   // row stride (halves) of kct / vct / tc / pc
 constexpr int AST = C + 4;   // row stride (floats) of aws
 
 struct Smem {
-    _Float16 kc[C * KST];     // k' = k / 2^E, token-major
-    _Float16 qc[C * KST];     // q' = q / 2^E, token-major
-    _Float16 kct[DK * TST];   // k', key-major
+    _Float16 kc[C * KST];     // unit keys k^, token-major
+    _Float16 qc[C * KST];     // q^ (or q / 2^E), token-major
+    _Float16 kct[DK * TST];   // unit keys, key-major
     uint16_t vct[DV * TST];   // v (bf16 bits), value-major
     _Float16 tc[C * TST];     // T scaled to fp16
-    _Float16 pc[C * TST];     // P_ts = e^{g_t-g_s} kap_s (q'_t . k'_s), s <= t
+    _Float16 pc[C * TST];     // P_ts = 2^{g_t-g_s} (q'_t . k^_s), s <= t
     float aws[C * AST];       // A, then T, in float32
     float wws[32 * 33];       // scratch for the blocked inverse
     alignas(16) float beta[C];
-    alignas(16) float g[C];               // ln alpha, then its chunk-local prefix sum
-    alignas(16) float egk[C];             // e^{g_t} kap_t
-    alignas(16) float eg[C];              // e^{g_t}
-    alignas(16) float kap[C];             // 2^E_t / ||k_t||
-    alignas(16) float kapq[C];            // 2^E_t / ||q_t|| (or 2^E_t)
-    alignas(16) float wsc[C];             // e^{g_C - g_t} kap_t
+    alignas(16) float g[C];               // log2 alpha, then its chunk-local prefix sum
+    alignas(16) float eg[C];              // 2^{g_t}
+    alignas(16) float kapq[C];            // 1, or 2^E_t for unnormalised queries
+    alignas(16) float wsc[C];             // 2^{g_C - g_t}
     float red[NW];
     float egC;
 };
+
+// Workgroup barrier that orders LDS traffic only: outstanding global loads
+// (the next chunk's prefetch) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -120,9 +130,32 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// lower-triangular 16x16 tiles (mt, nt) of a 64 x 64 matrix, nt <= mt
-__device__ __constant__ const int8_t kTileM[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__device__ __constant__ const int8_t kTileN[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// v_mfma_f32_16x16x16_f16: lane i holds A[i%16][4(i/16)+j] and B[4(i/16)+j][i%16];
+// its result D[4(i/16)+j][i%16] is laid out like a B operand.
+__device__ __forceinline__ floatx4 mfma1616(half4 a, half4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// A operand of mfma1616 from a float32 row-major block (rows r0.., cols c0..).
+__device__ __forceinline__ half4 a1616(const float *m, int stride, int r0, int c0, int lane) {
+    const float4 v = *reinterpret_cast<const float4 *>(m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4));
+    half4 h;
+    h[0] = (_Float16)v.x; h[1] = (_Float16)v.y; h[2] = (_Float16)v.z; h[3] = (_Float16)v.w;
+    return h;
+}
+
+// B operand of mfma1616 from a float32 row-major block.
+__device__ __forceinline__ half4 b1616(const float *m, int stride, int r0, int c0, int lane) {
+    const float *p = m + (r0 + 4 * (lane >> 4)) * stride + c0 + (lane & 15);
+    half4 h;
+    h[0] = (_Float16)p[0]; h[1] = (_Float16)p[stride]; h[2] = (_Float16)p[2 * stride]; h[3] = (_Float16)p[3 * stride];
+    return h;
+}
+
+// Lower-triangular 16x16 tiles (mt, nt), nt <= mt, of a 64 x 64 matrix,
+// enumerated 0..9 and packed 4 bits per entry (no memory lookup).
+__device__ __forceinline__ int tile_m(int idx) { return (int)((0x3333222110ull >> (4 * idx)) & 0xf); }
+__device__ __forceinline__ int tile_n(int idx) { return (int)((0x3210210100ull >> (4 * idx)) & 0xf); }
 
 
 // Store S (held as S^T tiles) to a d_v x d_k row-major float32 block.
@@ -144,46 +177,58 @@ __device__ __forceinline__ int chunk_len(const LaunchDesc &P, int len, int t0, i
     return lc;
 }
 
-// Raw loads of one chunk into registers.  Thread tid covers tokens
-// 16 i + tid/16 (i = 0..3) and elements 8 (tid%16) .. +7 of q, k and v;
-// threads 0..63 load alpha, threads 64..127 beta.  Rows past the chunk read
-// nothing and hold k = q = v = 0, alpha = 1, beta = 0.
-struct RawChunk {
-    uint4 k[4], q[4], v[4];
-    uint16_t a, b;
+// Raw bf16 rows of the next chunk, staged in LDS by direct global->LDS loads
+// (global_load_lds_dwordx4), so the prefetch holds no VGPRs and stays in
+// flight across LDS-only barriers.  Rows are 256 B, row-major.  The gates
+// (one bf16 per token) go through a register instead: a sub-dword LDS DMA
+// still writes one dword per lane.
+struct RawStage {
+    uint16_t k[C * DK];
+    uint16_t q[C * DK];
+    uint16_t v[C * DV];
 };
 
-__device__ __forceinline__ void load_chunk(RawChunk &R, const uint16_t *kg, const uint16_t *qg,
-                                           const uint16_t *vg, const uint16_t *ag, const uint16_t *bg,
-                                           int64_t row_base, int H, int h, int tid, int lc,
-                                           bool want_q) {
-    const int lrow = tid >> 4;
-    const int lcol = 8 * (tid & 15);
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+// Lane l of the wave copies `size` bytes from g to (LDS base) + l * size.
+__device__ __forceinline__ void dma16(const void *g, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((gvoid_t *)g, (lvoid_t *)lds_wave_base, 16, 0, 0);
+}
+
+// Queue the loads of one chunk of lc tokens starting at packed row row_base.
+// Wave w, step i copies rows 16 i + 4 w .. +3 (lane l: row + l/16, 16 B at
+// column 8 (l%16)); wave 0 loads alpha and wave 1 beta into `gate` (issued
+// first, so waiting for it leaves the copies in flight).  Rows at or past lc
+// are not read; the consumer treats them as k = q = v = 0, alpha = 1, beta = 0.
+__device__ __forceinline__ void dma_chunk(RawStage &R, uint16_t &gate, const uint16_t *kg,
+                                          const uint16_t *qg, const uint16_t *vg, const uint16_t *ag,
+                                          const uint16_t *bg, int64_t row_base, int H, int h, int w,
+                                          int lane, int lc, bool want_q) {
+    if (w < 2 && lane < lc) gate = (w == 0 ? ag : bg)[(row_base + lane) * H + h];
+    const int sub = lane >> 4;
+    const int col = 8 * (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int t = 16 * i + lrow;
-        if (t < lc) {
-            const int64_t rowi = (row_base + t) * H + h;
-            R.k[i] = *reinterpret_cast<const uint4 *>(kg + rowi * DK + lcol);
-            R.v[i] = *reinterpret_cast<const uint4 *>(vg + rowi * DV + lcol);
-            R.q[i] = want_q ? *reinterpret_cast<const uint4 *>(qg + rowi * DK + lcol) : make_uint4(0, 0, 0, 0);
-        } else {
-            R.k[i] = make_uint4(0, 0, 0, 0);
-            R.v[i] = make_uint4(0, 0, 0, 0);
-            R.q[i] = make_uint4(0, 0, 0, 0);
+        const int r0 = 16 * i + 4 * w;
+        if (r0 + sub < lc) {
+            const int64_t rowi = (row_base + r0 + sub) * H + h;
+            dma16(kg + rowi * DK + col, &R.k[r0 * DK]);
+            dma16(vg + rowi * DV + col, &R.v[r0 * DV]);
+            if (want_q) dma16(qg + rowi * DK + col, &R.q[r0 * DK]);
         }
     }
-    if (tid < C) {
-        R.a = tid < lc ? ag[(row_base + tid) * H + h] : (uint16_t)0x3f80;  // alpha = 1
-    } else if (tid < 2 * C) {
-        const int t = tid - C;
-        R.b = t < lc ? bg[(row_base + t) * H + h] : (uint16_t)0;          // beta = 0
-    }
+}
+
+// Wait for this wave's outstanding loads (the staged chunk), then barrier.
+__device__ __forceinline__ void vm_lds_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
 {
     __shared__ Smem sm;
+    __shared__ RawStage sraw;
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int h = L % P.H;
@@ -191,7 +236,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
     const int b = P.req[r];
     const int H = P.H;
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hi32 = lane >> 5;
@@ -246,28 +291,31 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
 
     // ---- raw loads of one chunk into registers: lane covers tokens 16i + tid/16
     // (i = 0..3) and elements 8*(tid%16) .. +7 of q, k and v.
-    RawChunk raw;
-    raw.a = 0x3f80;
-    raw.b = 0;
     const int lrow = tid >> 4;
     const int lcol = 8 * (tid & 15);
 
     int t0 = 0;
     int lc = len > 0 ? chunk_len(P, len, 0, ne, ne_end) : 0;
-    if (len > 0) load_chunk(raw, kg, qg, vg, ag, bg, row0, H, h, tid, lc, want_o);
+    uint16_t gate = 0;
+    if (len > 0) dma_chunk(sraw, gate, kg, qg, vg, ag, bg, row0, H, h, w, lane, lc, want_o);
 
     while (t0 < len) {
-        __syncthreads();  // previous chunk's LDS reads are done
+        vm_lds_barrier();  // staged chunk has landed; previous chunk's LDS reads are done
 
-        // ---- phase 1: per-token scales, fp16 operands into LDS ----------------
+        // ---- phase 1: unit keys / queries as fp16 operands into LDS ----------
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * i + lrow;
             float kf[8], qf[8];
-            const uint32_t kw[4] = {raw.k[i].x, raw.k[i].y, raw.k[i].z, raw.k[i].w};
-            const uint32_t qw[4] = {raw.q[i].x, raw.q[i].y, raw.q[i].z, raw.q[i].w};
-            const uint32_t vw[4] = {raw.v[i].x, raw.v[i].y, raw.v[i].z, raw.v[i].w};
-            float kss = 0.f, kmx = 0.f, qss = 0.f, qmx = 0.f;
+            const bool live = t < lc;
+            const uint4 z4 = make_uint4(0, 0, 0, 0);
+            const uint4 rk = live ? *reinterpret_cast<const uint4 *>(&sraw.k[t * DK + lcol]) : z4;
+            const uint4 rq = (live && want_o) ? *reinterpret_cast<const uint4 *>(&sraw.q[t * DK + lcol]) : z4;
+            const uint4 rv = live ? *reinterpret_cast<const uint4 *>(&sraw.v[t * DV + lcol]) : z4;
+            const uint32_t kw[4] = {rk.x, rk.y, rk.z, rk.w};
+            const uint32_t qw[4] = {rq.x, rq.y, rq.z, rq.w};
+            const uint32_t vw[4] = {rv.x, rv.y, rv.z, rv.w};
+            float kss = 0.f, qss = 0.f, qmx = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 kf[2 * e] = __uint_as_float(kw[e] << 16);
@@ -278,7 +326,6 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kss += kf[e] * kf[e];
-                kmx = fmaxf(kmx, fabsf(kf[e]));
                 qss += qf[e] * qf[e];
                 qmx = fmaxf(qmx, fabsf(qf[e]));
             }
@@ -286,17 +333,18 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
             for (int o = 1; o < 16; o <<= 1) {
                 kss += __shfl_xor(kss, o);
                 qss += __shfl_xor(qss, o);
-                kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-                qmx = fmaxf(qmx, __shfl_xor(qmx, o));
+                if (!norm_q) qmx = fmaxf(qmx, __shfl_xor(qmx, o));
             }
-            int Ek, Eq;
-            frexpf(kmx, &Ek);
-            frexpf(qmx, &Eq);
+            // k^ = k / ||k|| (a zero key stays zero); q^ likewise, or q / 2^E
+            const float ks = kss > 0.f ? rsqrtf(kss) : 0.f;
+            int Eq = 0;
+            if (!norm_q) frexpf(qmx, &Eq);
+            const float qs = norm_q ? (qss > 0.f ? rsqrtf(qss) : 0.f) : ldexpf(1.f, -Eq);
             half8 kh, qh;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                kh[e] = (_Float16)ldexpf(kf[e], -Ek);
-                qh[e] = (_Float16)ldexpf(qf[e], -Eq);
+                kh[e] = (_Float16)(kf[e] * ks);
+                qh[e] = (_Float16)(qf[e] * qs);
             }
             _Float16 *kp = &sm.kc[t * KST + lcol];
             _Float16 *qp = &sm.qc[t * KST + lcol];
@@ -311,25 +359,14 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
                 sm.vct[(lcol + 2 * e) * TST + t] = (uint16_t)(vw[e] & 0xffffu);
                 sm.vct[(lcol + 2 * e + 1) * TST + t] = (uint16_t)(vw[e] >> 16);
             }
-            if ((tid & 15) == 0) {
-                sm.kap[t] = kss > 0.f ? ldexpf(1.f, Ek) / sqrtf(kss) : 0.f;
-                sm.kapq[t] = norm_q ? (qss > 0.f ? ldexpf(1.f, Eq) / sqrtf(qss) : 0.f) : ldexpf(1.f, Eq);
-            }
+            if ((tid & 15) == 0) sm.kapq[t] = norm_q ? 1.f : ldexpf(1.f, Eq);
         }
         if (tid < C) {
-            sm.g[tid] = logf(fmaxf(bf(raw.a), 1e-30f));
+            sm.g[tid] = tid < lc ? log2_(fmaxf(bf(gate), 1e-30f)) : 0.f;
         } else if (tid < 2 * C) {
-            sm.beta[tid - C] = bf(raw.b);
+            sm.beta[tid - C] = tid - C < lc ? bf(gate) : 0.f;
         }
-
-        // prefetch the next chunk while this one is processed
-        const int t0n = t0 + lc;
-        int nen = ne;
-        if (nen < ne_end && P.emit_after[nen] == t0n) ++nen;
-        const int lcn = t0n < len ? chunk_len(P, len, t0n, nen, ne_end) : 0;
-        if (lcn > 0) load_chunk(raw, kg, qg, vg, ag, bg, row0 + t0n, H, h, tid, lcn, want_o);
-
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 2: decay prefix sums (wave 0) and the key/query Gram tiles --
         if (w == 0) {
@@ -340,12 +377,10 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
                 if (lane >= o) x += y;
             }
             const float gC = __shfl(x, 63);
-            const float e = expf(x);
             sm.g[lane] = x;
-            sm.eg[lane] = e;
-            sm.egk[lane] = e * sm.kap[lane];
-            sm.wsc[lane] = expf(gC - x) * sm.kap[lane];
-            if (lane == 0) sm.egC = expf(gC);
+            sm.eg[lane] = exp2_(x);
+            sm.wsc[lane] = exp2_(gC - x);
+            if (lane == 0) sm.egC = exp2_(gC);
         }
         floatx4 gacc[5];
 #pragma unroll
@@ -353,7 +388,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
             const int item = w + 4 * it;
             const int idx = item % 10;
             const _Float16 *src = item < 10 ? sm.kc : sm.qc;
-            const int mt = kTileM[idx], nt = kTileN[idx];
+            const int mt = tile_m(idx), nt = tile_n(idx);
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -364,28 +399,29 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
             }
             gacc[it] = acc;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int it = 0; it < 5; ++it) {
             const int item = w + 4 * it;
             const int idx = item % 10;
-            const int mt = kTileM[idx], nt = kTileN[idx];
+            const int mt = tile_m(idx), nt = tile_n(idx);
             const int s = 16 * nt + (lane & 15);
-            const float gs = sm.g[s], ks_ = sm.kap[s];
+            const float gs = sm.g[s];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * mt + 4 * (lane >> 4) + j;
-                const float dec = expf(sm.g[t] - gs);
+                const float dec = exp2_(sm.g[t] - gs);
                 if (item < 10) {
-                    sm.aws[t * AST + s] = s < t ? sm.beta[t] * dec * sm.kap[t] * ks_ * gacc[it][j] : 0.f;
+                    sm.aws[t * AST + s] = s < t ? sm.beta[t] * dec * gacc[it][j] : 0.f;
                 } else {
-                    sm.pc[t * TST + s] = (_Float16)(s <= t ? dec * ks_ * gacc[it][j] : 0.f);
+                    sm.pc[t * TST + s] = (_Float16)(s <= t ? dec * gacc[it][j] : 0.f);
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- phase 3: T = (I + A)^{-1} in float32 (blocked, in place) ---------
+        // ---- phase 3: T = (I + A)^{-1} (blocked, in place in aws) -------------
+        // 16 x 16 diagonal blocks: forward substitution in float32, one column per lane
         if (lane < 16) {
             const int bo = 16 * w;
             float x[16];
@@ -400,53 +436,42 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) sm.aws[(bo + rr) * AST + bo + lane] = x[rr];
         }
-        __syncthreads();
-        {   // 32 x 32 blocks: T10 = -T11 A10 T00, for p = 0, 1
-            const int p = tid >> 7, e = tid & 127;
-            const int rr = e >> 3, cc = 2 * (e & 7);
-            const int R1 = 32 * p + 16, C0 = 32 * p;
-            float w0 = 0.f, w1 = 0.f;
+        lds_barrier();
+        // 32 x 32 blocks p = 0, 1: T10 = -T11 (A10 T00), waves 0 and 1
+        if (w < 2) {
+            const int R1 = 32 * w + 16, C0 = 32 * w;
+            const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+            const floatx4 W4 = mfma1616(a1616(sm.aws, AST, R1, C0, lane), b1616(sm.aws, AST, C0, C0, lane), z4);
+            half4 wf;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const float a = sm.aws[(R1 + rr) * AST + C0 + k];
-                w0 += a * sm.aws[(C0 + k) * AST + C0 + cc];
-                w1 += a * sm.aws[(C0 + k) * AST + C0 + cc + 1];
-            }
-            sm.wws[p * 16 * 17 + rr * 17 + cc] = w0;
-            sm.wws[p * 16 * 17 + rr * 17 + cc + 1] = w1;
-            __syncthreads();
-            float x0 = 0.f, x1 = 0.f;
-            for (int k = 0; k <= rr; ++k) {
-                const float t = sm.aws[(R1 + rr) * AST + R1 + k];
-                x0 += t * sm.wws[p * 16 * 17 + k * 17 + cc];
-                x1 += t * sm.wws[p * 16 * 17 + k * 17 + cc + 1];
-            }
-            sm.aws[(R1 + rr) * AST + C0 + cc] = -x0;
-            sm.aws[(R1 + rr) * AST + C0 + cc + 1] = -x1;
+            for (int j = 0; j < 4; ++j) wf[j] = (_Float16)W4[j];
+            const floatx4 X4 = mfma1616(a1616(sm.aws, AST, R1, R1, lane), wf, z4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sm.aws[(R1 + 4 * (lane >> 4) + j) * AST + C0 + (lane & 15)] = -X4[j];
         }
-        __syncthreads();
-        {   // 64 x 64: T10 = -T11 A10 T00 with 32 x 32 blocks
-            const int rr = tid >> 3, cc = 4 * (tid & 7);
-            float wv[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k < 32; ++k) {
-                const float a = sm.aws[(32 + rr) * AST + k];
+        lds_barrier();
+        // 64 x 64: T10 = -T11 (A10 T00) with 32 x 32 blocks; wave w owns the
+        // 16 x 16 output block (rb, cb) = (w / 2, w % 2)
+        {
+            const int rb = w >> 1, cb = w & 1;
+            floatx4 W4 = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = cb; kb < 2; ++kb)
+                W4 = mfma1616(a1616(sm.aws, AST, 32 + 16 * rb, 16 * kb, lane),
+                              b1616(sm.aws, AST, 16 * kb, 16 * cb, lane), W4);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (k >= cc + q) wv[q] += a * sm.aws[k * AST + cc + q];
-            }
+            for (int j = 0; j < 4; ++j)
+                sm.wws[(16 * rb + 4 * (lane >> 4) + j) * 33 + 16 * cb + (lane & 15)] = W4[j];
+            lds_barrier();
+            floatx4 X4 = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb <= rb; ++kb)
+                X4 = mfma1616(a1616(sm.aws, AST, 32 + 16 * rb, 32 + 16 * kb, lane),
+                              b1616(sm.wws, 33, 16 * kb, 16 * cb, lane), X4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sm.wws[rr * 33 + cc + q] = wv[q];
-            __syncthreads();
-            float xv[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k <= rr; ++k) {
-                const float t = sm.aws[(32 + rr) * AST + 32 + k];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) xv[q] += t * sm.wws[k * 33 + cc + q];
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sm.aws[(32 + rr) * AST + cc + q] = -xv[q];
+            for (int j = 0; j < 4; ++j)
+                sm.aws[(32 + 16 * rb + 4 * (lane >> 4) + j) * AST + 16 * cb + (lane & 15)] = -X4[j];
         }
-        __syncthreads();
+        lds_barrier();
         {   // T -> fp16 with a power-of-two scale
             float mx = 0.f;
 #pragma unroll 4
@@ -457,7 +482,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
             }
             mx = wave_max(mx);
             if (lane == 0) sm.red[w] = mx;
-            __syncthreads();
+            lds_barrier();
             mx = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
             const float sc = ldexpf(1.f, fp16_exp(mx));
 #pragma unroll 4
@@ -467,9 +492,18 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
                 sm.tc[t * TST + s] = (_Float16)(s <= t ? sm.aws[t * AST + s] * sc : 0.f);
             }
         }
-        __syncthreads();
+        lds_barrier();
         const float unT = ldexpf(1.f, -fp16_exp(fmaxf(fmaxf(sm.red[0], sm.red[1]),
                                                        fmaxf(sm.red[2], sm.red[3]))));
+
+        // The staging area was consumed in phase 1: queue the next chunk now, so
+        // that its copies overlap the state chain (queued any earlier, LDS reads
+        // of phase 3 would have to wait for them).
+        const int t0n = t0 + lc;
+        int nen = ne;
+        if (nen < ne_end && P.emit_after[nen] == t0n) ++nen;
+        const int lcn = t0n < len ? chunk_len(P, len, t0n, nen, ne_end) : 0;
+        if (lcn > 0) dma_chunk(sraw, gate, kg, qg, vg, ag, bg, row0 + t0n, H, h, w, lane, lcn, want_o);
 
         // ---- phase 4: the state chain of wave w (value rows 32w .. 32w+31) ----
         const int dv = 32 * w + l32;
@@ -486,7 +520,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
             Sf[a][0] = to_frag(Sacc[a], 0, scS);
             Sf[a][1] = to_frag(Sacc[a], 1, scS);
         }
-        // Y = K' S0'^T and Z = Q' S0'^T (tokens x value rows of this wave)
+        // Y = K^ S0'^T and Z = Q' S0'^T (tokens x value rows of this wave)
         floatx16 Y[2], Z[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -502,7 +536,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
             Y[u] = acc;
             Z[u] = zacc;
         }
-        // B_t = beta_t (v_t - e^{g_t} kap_t S0 k'_t)
+        // B_t = beta_t (v_t - 2^{g_t} S0 k^_t)
         float bmx = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -511,7 +545,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
                 const int t = 32 * u + 8 * q4 + 4 * hi32;
                 const uint2 v2 = *reinterpret_cast<const uint2 *>(&sm.vct[dv * TST + t]);
                 const float4 bt = *reinterpret_cast<const float4 *>(&sm.beta[t]);
-                const float4 ek = *reinterpret_cast<const float4 *>(&sm.egk[t]);
+                const float4 ek = *reinterpret_cast<const float4 *>(&sm.eg[t]);
                 const float vv[4] = {__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u),
                                      __uint_as_float(v2.y << 16), __uint_as_float(v2.y & 0xffff0000u)};
                 const float bb[4] = {bt.x, bt.y, bt.z, bt.w};
@@ -550,7 +584,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
             }
             U[u2] = acc;
         }
-        // outputs o_t = kapq_t (e^{g_t} S0 q'_t + sum_s P_ts u_s)
+        // outputs o_t = kapq_t (2^{g_t} S0 q'_t + sum_s P_ts u_s)
         if (want_o) {
             const int eU = fp16_exp(wave_max(umx));
             const float scU = ldexpf(1.f, eU), unU = ldexpf(1.f, -eU);
@@ -586,7 +620,7 @@ __global__ __launch_bounds__(NT, 1) void chunked_kernel(const LaunchDesc P)
                 }
             }
         }
-        // S_C = e^{g_C} S0 + sum_s (e^{g_C - g_s} kap_s u_s) k'_s^T
+        // S_C = 2^{g_C} S0 + sum_s (2^{g_C - g_s} u_s) k^_s^T
         float wmx = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
