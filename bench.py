@@ -30,6 +30,22 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
 
 
+def measured_traffic(kernel_src: str, profile: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        txt = open(profile).read()
+        sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    vals = dict(l.split(":", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes_per_launch:",
+                                                                            "kernel_source_sha256_prefix:")))
+    if vals.get("kernel_source_sha256_prefix", "").strip() != sha:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
 def algorithmic_bytes(token_heads: int, pairs: int, dk: int, dv: int, elem: int,
                       with_o: bool = True) -> int:
     """Bytes a replay must move: q, k, v, alpha, beta in; o out; final state out."""
@@ -90,6 +106,9 @@ def main():
     ap.add_argument("--kernel", choices=["auto", "recurrent", "chunked"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-output", action="store_true", help="skip o (state only)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the replay, time a plain device copy of this many MiB "
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -105,6 +124,9 @@ def main():
     gdn.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mib:
+        copy_probe(torch, dev, args)
+        return
     w = W.config(3, device=dev)
     flags = w.flags | {"auto": 0, "recurrent": gdn.KERNEL_RECURRENT,
                        "chunked": gdn.KERNEL_CHUNKED}[args.kernel]
@@ -156,7 +178,9 @@ def main():
         roof = {"bound": "alu", "achieved": nflops / (kern_ms * 1e-3) / 1e12,
                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = (measured_traffic(os.path.join(ROOT, "gated_delta_rule_scan_amd", "csrc", "gdn_chunked.hip"),
+                                        os.path.join(ROOT, "profiles", "chunked_kernel_tail5pct_traffic.md"))
+                       if chunked and o is not None else None)
     roof["algorithmic_bytes_per_launch"] = nbytes
     roof["algorithmic_flops_per_launch"] = nflops
     roof["kernel_ms"] = kern_ms
@@ -185,6 +209,25 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, spans)
     print(json.dumps(out), flush=True)
+
+
+def copy_probe(torch, dev, args):
+    """A plain copy of known size: one read and one write of n bytes per launch."""
+    n = args.copy_probe_mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "ms": ms,
+                      "GB/s_read+write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 if __name__ == "__main__":
