@@ -8,33 +8,48 @@
 // S_{t-1} k_t), unrolling eq. (1) gives
 //     S_t = 2^{g_t} S_0 + sum_{s<=t} 2^{g_t - g_s} u_s k_s^T,
 // and the u_t solve a unit lower-triangular system
-//     (I + A) U = B,  A_ts = beta_t 2^{g_t - g_s} (k_t . k_s)  (s < t),
-//                     B_t  = beta_t (v_t - 2^{g_t} S_0 k_t),
+//     (I + A) U = diag(beta) B~,  A_ts = beta_t 2^{g_t - g_s} (k_t . k_s)  (s < t),
+//                                 B~_t = v_t - 2^{g_t} S_0 k_t,
 // so that, with T = (I + A)^{-1} (it depends on keys and gates only):
-//     U   = T B
+//     U   = (T diag(beta)) B~
 //     o_t = 2^{g_t} S_0 q_t + sum_{s<=t} 2^{g_t - g_s} (q_t . k_s) u_s
 //     S_C = 2^{g_C} S_0 + sum_s 2^{g_C - g_s} u_s k_s^T.
 // This is the compact-WY way of applying a product of rank-1 modifications of
 // the identity (Golub & Van Loan, Matrix Computations, §5.1) to the chunk.
 //
-// Precision: the dense products run on fp16 MFMA with float32 accumulation.
-// Keys are unit vectors (|k_i| <= 1 fits fp16 as is); queries are normalised
-// too, or scaled per token by an exact power of two.  The state, B, U and T
-// are scaled by exact powers of two before rounding to fp16.  T is formed
-// blockwise: the two 16 x 16 diagonal blocks by float32 substitution, the
-// off-diagonal block by one doubling step on MFMA.  The state itself never
-// leaves float32; it is held as S = 2^sig * Sacc with a per-wave exponent sig,
-// so that each chunk rescales it once.
+// Key side (state independent, one chunk ahead of the state chain):
+//  - all waves convert the next chunk's keys/queries to unit fp16 rows;
+//  - wave 0 forms T entirely in registers: the Gram tiles come out of MFMA in
+//    accumulator layout, and because the Gram matrix is symmetric both A and
+//    A^T are available elementwise.  The 8 x 8 diagonal blocks are inverted in
+//    the product form (I + N)^{-1} = (I - N)(I + N^2)(I + N^4) (N^8 = 0), then
+//    two doubling steps X_10 = -X_11 A_10 X_00 give the 16 x 16 and 32 x 32
+//    inverse.  An MFMA A operand of X is X^T in accumulator layout, so X and
+//    X^T are carried side by side where needed;
+//  - wave 1 forms P_ts = 2^{g_t - g_s} (q_t . k_s).
+// State side (each wave owns 32 value rows): the state is kept transposed
+// (S^T, d_k x d_v) in v_mfma_f32_32x32x16_f16 accumulator layout, fp32, as
+// S = 2^{-sigma} Sacc.  The decay 2^{g_C} of a chunk is folded into sigma
+// rather than applied to Sacc; Sacc is rescaled only when a running bound on
+// max|Sacc| leaves the fp16 band.  The accumulator slots feed back as MFMA B
+// operands (their reduction index is permuted the same way on both operands).
+//
+// Operands that the MFMA wants "down a column" (K^T for the state update, V,
+// T and P as A operands) are read with ds_read_b64_tr_b16 from token-major LDS
+// tiles, so nothing is written transposed.  Keys/queries are stored with the
+// middle two 4-column groups of every 16 columns swapped, so that a lane's
+// 8-element fragment of the permuted reduction order is one 16-byte read, and
+// with the 16-byte units of each row XOR-swizzled against bank conflicts.
+//
+// Precision: products run on fp16 MFMA with float32 accumulation.  Every fp16
+// operand is kept inside the fp16 normal range by exact power-of-two scales
+// (checked per chunk; the common case needs none).  The state never leaves
+// float32.
 //
 // Work split: one workgroup of 4 waves per (request, head), two workgroups per
-// CU (LDS ~70 KB each).  Wave w owns value rows [32w, 32w + 32).  The state is
-// kept transposed, S^T (d_k x d_v), in MFMA accumulator layout; because the
-// reduction index of an MFMA may be permuted freely (as long as both operands
-// agree), each wave feeds its own accumulators back as B fragments of the
-// next chunk's products, so a wave's chunk-to-chunk chain never touches LDS
-// for the state.  Wave 0 also forms T while the other waves start the
-// state-dependent products.  The next chunk's q/k/v rows are copied into LDS
-// with global_load_lds_dwordx4 while the current chunk runs.
+// CU (LDS ~68 KB each).  V rows of a chunk are copied into LDS with
+// global_load_lds_dwordx4 two chunks ahead, each wave copying its own value
+// columns; key/query rows are prefetched into registers one chunk ahead.
 #include "gdn_launch.h"
 #include "gdn_numeric.h"
 
@@ -45,56 +60,59 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+typedef __attribute__((address_space(3))) void lvoid_t;
 
 constexpr int C = 32;        // tokens per chunk
 constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;
-constexpr int KST = DK + 4;  // row stride (halves) of kc / qc
-constexpr int TST = C + 4;   // row stride (halves) of kct / vct / tc / pc
-constexpr int AST = C + 4;   // row stride (floats) of aws
+constexpr int NVB = 3;       // V staging buffers (copies run two chunks ahead)
 
 struct Smem {
-    alignas(16) uint16_t rk[C * DK];   // raw bf16 rows of the next chunk (LDS DMA)
-    alignas(16) uint16_t rq[C * DK];
-    alignas(16) uint16_t rv[C * DV];
-    alignas(16) _Float16 kc[C * KST];  // unit keys, token-major
-    alignas(16) _Float16 qc[C * KST];  // q^ (or q / 2^E), token-major
-    alignas(16) _Float16 kct[DK * TST];  // unit keys, key-major
-    alignas(16) uint16_t vct[DV * TST];  // v (bf16 bits), value-major; then o staging
-    alignas(16) _Float16 tc[C * TST];  // T scaled to fp16
-    alignas(16) _Float16 pc[C * TST];  // P_ts = 2^{g_t - g_s} (q'_t . k_s), s <= t
-    alignas(16) float aws[C * AST];    // A, then T, in float32
-    alignas(16) float atd[2 * 16 * 16];  // diagonal 16x16 blocks of A, transposed
-    alignas(16) float beta[C];
-    alignas(16) float g[C];            // log2 alpha, then its chunk-local prefix sum
-    alignas(16) float eg[C];           // 2^{g_t}
-    alignas(16) float wsc[C];          // 2^{g_C - g_t}
-    alignas(16) float kapq[C];         // 1, or 2^E_t for unnormalised queries
-    float unT;
+    alignas(16) _Float16 kh[2][C * DK];  // unit keys, fp16 (layout: kofs)
+    alignas(16) _Float16 qh[2][C * DK];  // q^ (or q / 2^E), fp16 (layout: kofs)
+    alignas(16) uint16_t vr[NVB][NW][C * 32];  // raw bf16 v: [wave][token][32 value columns]
+    alignas(16) _Float16 tT[2][C * C];   // (T diag(beta))^T * 2^eT, row s, column t
+    alignas(16) _Float16 pT[2][C * C];   // P^T, row s, column t
+    alignas(16) float gl[2][C];          // chunk-local prefix sum of log2 alpha
+    alignas(16) float be[2][C];          // beta (0 past the chunk)
+    alignas(16) float eg[2][C];          // 2^{g_t}
+    alignas(16) float ws[2][C];          // 2^{g_C - g_t}
+    alignas(16) float kq[2][C];          // 1, or 2^{E_t} for unnormalised queries
+    alignas(16) float cw[NW][4][C];      // per-wave coefficients (see the state side)
+    float gC[2];
+    float tsc[2];                        // 2^{-eT}
 };
 
-// Workgroup barrier ordering LDS traffic only: outstanding global loads
-// (the next chunk's copies) stay in flight across it.
+// ---- LDS layouts -------------------------------------------------------------
+// kh/qh element (token t, stored column sc): 16-byte unit sc/8 of row t is
+// placed at unit (sc/8) ^ swz(t).  Actual column c is stored at
+// 16 (c/16) + 4 sqd((c/4) % 4) + c % 4 (the middle 4-column groups swapped).
+__device__ __forceinline__ int swz(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
+__device__ __forceinline__ int sqd(int q) { return ((q & 1) << 1) | (q >> 1); }
+__device__ __forceinline__ int kofs(int t, int unit, int h) { return t * DK + ((unit ^ swz(t)) << 3) + h; }
+
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// Wait for this wave's outstanding loads (the staged chunk), then barrier.
-__device__ __forceinline__ void vm_lds_barrier() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
 
-// Cross-lane steps on the VALU (DPP) rather than through LDS.
 template <int CTRL, int ROWMASK = 0xf>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK,
                                                                   0xf, true));
 }
-// Sum / max over each row of 16 lanes; every lane gets its row's result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, true);
+}
 __device__ __forceinline__ float row16_sum(float x) {
     x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
     x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
@@ -112,10 +130,12 @@ __device__ __forceinline__ float row16_max(float x) {
 __device__ __forceinline__ float lane_val(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
-// Maximum over the wave, as a wave-uniform value (all lanes must be active).
+// Maximum over the wave of non-negative values (all lanes active), uniform.
 __device__ __forceinline__ float wave_max(float x) {
     x = row16_max(x);
-    return fmaxf(fmaxf(lane_val(x, 0), lane_val(x, 16)), fmaxf(lane_val(x, 32), lane_val(x, 48)));
+    const uint32_t a = __float_as_uint(lane_val(x, 0)), b = __float_as_uint(lane_val(x, 16));
+    const uint32_t c = __float_as_uint(lane_val(x, 32)), d = __float_as_uint(lane_val(x, 48));
+    return __uint_as_float(max(max(a, b), max(c, d)));
 }
 // Inclusive prefix sum over lanes 0..31 (row_shr within rows, then row_bcast:15).
 __device__ __forceinline__ float scan32(float x) {
@@ -127,39 +147,41 @@ __device__ __forceinline__ float scan32(float x) {
     return x;
 }
 
-// Power-of-two exponent e bringing max|x| into [2^14, 2^15) (x * 2^e fits fp16).
-__device__ __forceinline__ int fp16_exp(float mx) {
+// Power-of-two exponent e for an fp16 operand with maximum magnitude mx: 0 when
+// mx is already in [2^-6, 2^14), else the one bringing mx into [2^7, 2^8).
+__device__ __forceinline__ int f16_adjust(float mx) {
+    if (!(mx > 0.f) || (mx >= 0x1p-6f && mx < 0x1p14f)) return 0;
     int E;
     frexpf(mx, &E);
-    return 15 - E;
+    return 8 - E;
 }
 
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_to_f32(b); }
+__device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ half4 ld4(const _Float16 *p) {
-    return *reinterpret_cast<const half4 *>(p);
+__device__ __forceinline__ half8 ld8(const _Float16 *p) { return *reinterpret_cast<const half8 *>(p); }
+__device__ __forceinline__ half8 cat(half4 a, half4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+
+// 4 halves of a 16-lane transposed read: lane n of each 16-lane group gets
+// element n % 4 of the 8 bytes addressed by lane 4 j + n / 4, for j = 0..3.
+__device__ __forceinline__ half4 tr4(const _Float16 *p) {
+    return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(p)));
+}
+__device__ __forceinline__ i16x4_t tr4u(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
-// A fragment of v_mfma_f32_32x32x16_f16 from a row-major fp16 tile with the
-// reduction index permuted: lane i takes row `row`, columns
-// c0 + 4*(i/32) + {0..3} and c0 + 8 + 4*(i/32) + {0..3}.  This matches the
-// order in which a 32 x 32 accumulator holds its rows (see to_frag).
-__device__ __forceinline__ half8 frag_perm(const _Float16 *base, int stride, int row, int c0, int lane) {
-    const _Float16 *p = base + row * stride + c0 + 4 * (lane >> 5);
-    const half4 lo = ld4(p), hi = ld4(p + 8);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+__device__ __forceinline__ half4 h4(floatx4 x) {
+    half4 r;
+    r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
+    return r;
 }
-
-__device__ __forceinline__ half8 frag_contig(const _Float16 *p) {
-    const half4 lo = ld4(p), hi = ld4(p + 4);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Slots 8*hf .. 8*hf+7 of a 32x32 accumulator, scaled, as an fp16 B fragment.
-__device__ __forceinline__ half8 to_frag(const floatx16 &acc, int hf, float scale) {
+// Slots 8*hf .. 8*hf+7 of a 32x32 accumulator as an fp16 B fragment.
+__device__ __forceinline__ half8 to_frag(const floatx16 &acc, int hf) {
     half8 r;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (_Float16)(acc[8 * hf + j] * scale);
+    for (int j = 0; j < 8; ++j) r[j] = (_Float16)acc[8 * hf + j];
     return r;
 }
 
@@ -170,37 +192,20 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 // v_mfma_f32_16x16x16_f16: lane i holds A[i%16][4(i/16)+j] and B[4(i/16)+j][i%16];
-// its result D[4(i/16)+j][i%16] is laid out like a B operand.
-__device__ __forceinline__ floatx4 mfma1616(half4 a, half4 b, floatx4 c) {
+// D[4(i/16)+j][i%16] is laid out like B, so the A operand of a matrix X is
+// X^T in accumulator layout.
+__device__ __forceinline__ floatx4 mm16(half4 a, half4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
-// A operand of mfma1616 from a float32 row-major block (rows r0.., cols c0..).
-__device__ __forceinline__ half4 a1616(const float *m, int stride, int r0, int c0, int lane) {
-    const float4 v = *reinterpret_cast<const float4 *>(m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4));
-    half4 h;
-    h[0] = (_Float16)v.x; h[1] = (_Float16)v.y; h[2] = (_Float16)v.z; h[3] = (_Float16)v.w;
-    return h;
-}
-// B operand of mfma1616 from a float32 row-major block.
-__device__ __forceinline__ half4 b1616(const float *m, int stride, int r0, int c0, int lane) {
-    const float *p = m + (r0 + 4 * (lane >> 4)) * stride + c0 + (lane & 15);
-    half4 h;
-    h[0] = (_Float16)p[0]; h[1] = (_Float16)p[stride]; h[2] = (_Float16)p[2 * stride]; h[3] = (_Float16)p[3 * stride];
-    return h;
-}
 
-typedef __attribute__((address_space(3))) void lvoid_t;
-
-// Lane l of the wave copies 16 bytes from base + voff (bytes) to
-// (LDS base) + 16 l (global_load_lds_dwordx4 with an SGPR base; the LDS base
-// goes in M0).  Issued as inline assembly so that the compiler does not order
-// later LDS reads of other buffers behind it: the only wait for these copies
-// is the explicit vmcnt(0) at the top of the next chunk.
 __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
+// Lane l copies 16 bytes from base + voff to (LDS base) + 16 l.  Inline
+// assembly with an SGPR base, so that the compiler neither waits for it nor
+// orders LDS accesses of other buffers behind it.
 __device__ __forceinline__ void dma16(uint64_t base, uint32_t voff, void *lds_wave_base) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)lds_wave_base));
@@ -208,45 +213,305 @@ __device__ __forceinline__ void dma16(uint64_t base, uint32_t voff, void *lds_wa
                  :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
-// Chunk schedule: up to C tokens, cut at the next emission position.
+// ---- chunk schedule ------------------------------------------------------------
+struct Chunk {
+    int t0, lc, ne;  // first position, length (0: none), first emission not yet taken
+};
 __device__ __forceinline__ int chunk_len(const LaunchDesc &P, int len, int t0, int e, int e_end) {
     int lc = min(C, len - t0);
     if (e < e_end) lc = min(lc, P.emit_after[e] - t0);
     return lc;
 }
+__device__ __forceinline__ Chunk next_chunk(const LaunchDesc &P, const Chunk &c, int len, int ne_end) {
+    Chunk n;
+    n.t0 = c.t0 + c.lc;
+    n.ne = c.ne;
+    if (n.ne < ne_end && P.emit_after[n.ne] == n.t0) ++n.ne;
+    n.lc = (c.lc > 0 && n.t0 < len) ? chunk_len(P, len, n.t0, n.ne, ne_end) : 0;
+    return n;
+}
 
-// Queue the loads of one chunk of lc tokens starting at packed row row_base.
-// Wave w, step i copies rows 16 i + 4 w .. +3 (lane l: row + l/16, 16 B at
-// column 8 (l%16)); wave 0 loads alpha and wave 1 beta into `gate` first (a
-// sub-dword LDS copy would still write a dword per lane).  Rows at or past lc
-// are not read; the consumer treats them as k = q = v = 0, alpha = 1, beta = 0.
-__device__ __forceinline__ void dma_chunk(Smem &sm, uint16_t &gate, const uint16_t *kg,
-                                          const uint16_t *qg, const uint16_t *vg, const uint16_t *ag,
-                                          const uint16_t *bg, int64_t row_base, int H, int h, int w,
-                                          int lane, int lc, bool want_q) {
-    if (w < 2 && lane < lc) gate = (w == 0 ? ag : bg)[(row_base + lane) * H + h];
-    const int sub = lane >> 4;
-    const int64_t e0 = (row_base * H + h) * DK;  // element offset of the chunk's first row
-    const uint64_t kb = uniform64(reinterpret_cast<uint64_t>(kg + e0));
-    const uint64_t qb = uniform64(reinterpret_cast<uint64_t>(qg + e0));
-    const uint64_t vb = uniform64(reinterpret_cast<uint64_t>(vg + e0));
+// ---- loads ---------------------------------------------------------------------
+struct Pref {
+    uint4 k[2], q[2];  // raw bf16: rows 16 i + tid/16, columns 8 (tid%16) .. +7
+    uint16_t gate;     // wave 0: alpha (lanes 0..31), beta (lanes 32..63)
+};
+
+// Rows past the chunk are clamped to its last row (always in the span), so
+// that every load is issued; their values are ignored by the consumers.
+__device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t rowbase, int lc, int H, int h,
+                                        int tid, int w, int lane, bool want_q) {
+    const uint16_t *kg = static_cast<const uint16_t *>(P.k);
+    const uint16_t *qg = static_cast<const uint16_t *>(P.q);
 #pragma unroll
-    for (int i = 0; i < C / 16; ++i) {
-        const int r0 = 16 * i + 4 * w;
-        if (r0 + sub < lc) {
-            const uint32_t off = (uint32_t)(((r0 + sub) * H * DK + 8 * (lane & 15)) * 2);
-            dma16(kb, off, &sm.rk[r0 * DK]);
-            dma16(vb, off, &sm.rv[r0 * DV]);
-            if (want_q) dma16(qb, off, &sm.rq[r0 * DK]);
-        }
+    for (int i = 0; i < 2; ++i) {
+        const int t = min(16 * i + (tid >> 4), lc - 1);
+        const int64_t off = ((rowbase + t) * H + h) * DK + 8 * (tid & 15);
+        pf.k[i] = *reinterpret_cast<const uint4 *>(kg + off);
+        if (want_q) pf.q[i] = *reinterpret_cast<const uint4 *>(qg + off);
+    }
+    if (w == 0) {
+        const uint16_t *src = static_cast<const uint16_t *>(lane < 32 ? P.alpha : P.beta);
+        pf.gate = src[(rowbase + min(lane & 31, lc - 1)) * H + h];
     }
 }
 
-// Store S = 2^sig * Sacc (held as S^T tiles) to a d_v x d_k row-major block.
-__device__ __forceinline__ void store_state(float *dst_head, const floatx16 (&Sacc)[4], int sig, int w,
+// V rows of a chunk into the wave's slice of buffer vb: copy k covers rows
+// 16 k .. 16 k + 15, lane l taking row 16 k + l/4, value columns
+// 32 w + 8 (l%4) .. +7 (LDS: slice + 1 KiB k + 16 l).
+__device__ __forceinline__ void dma_v(Smem &sm, int vb, const LaunchDesc &P, int64_t rowbase, int lc, int H,
+                                      int h, int w, int lane) {
+    const uint16_t *vg = static_cast<const uint16_t *>(P.v);
+    const uint64_t base = uniform64(reinterpret_cast<uint64_t>(vg + (rowbase * H + h) * DV + 32 * w));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int row = min(16 * k + (lane >> 2), lc - 1);
+        const uint32_t voff = (uint32_t)((row * H * DV + 8 * (lane & 3)) * 2);
+        dma16(base, voff, &sm.vr[vb][w][16 * k * 32]);
+    }
+}
+
+// ---- key side, part 1 (all waves): fp16 unit keys / queries and gate sums -----
+__device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 raw, bool live, bool normalise,
+                                            float *kq_out) {
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = live ? bflo(wd[e]) : 0.f;
+        f[2 * e + 1] = live ? bfhi(wd[e]) : 0.f;
+    }
+    float sc;
+    if (normalise) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+        ss = row16_sum(ss);  // one token row per 16 lanes
+        sc = ss > 0.f ? rsqrtf(ss) : 0.f;
+    } else {
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+        mx = row16_max(mx);
+        int E = 0;
+        frexpf(mx, &E);
+        sc = ldexpf(1.f, -E);
+        if (kq_out) *kq_out = ldexpf(1.f, E);
+    }
+    half4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = (_Float16)(f[e] * sc);
+        hi[e] = (_Float16)(f[4 + e] * sc);
+    }
+    // actual 4-column groups 2(u%2), 2(u%2)+1 of 16-group u/2 -> stored groups u%2, 2 + u%2
+    const int g16 = u >> 1, h0 = 4 * (u & 1);
+    *reinterpret_cast<half4 *>(dst + kofs(t, 2 * g16, h0)) = lo;
+    *reinterpret_cast<half4 *>(dst + kofs(t, 2 * g16 + 1, h0)) = hi;
+}
+
+__device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &pf, int lc, int tid, int w,
+                                                 int lane, bool want_q, bool norm_q) {
+    const int u = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = 16 * i + (tid >> 4);
+        const bool live = t < lc;
+        convert_row(sm.kh[pb], t, u, pf.k[i], live, true, nullptr);
+        if (want_q) {
+            float kqv = 1.f;
+            convert_row(sm.qh[pb], t, u, pf.q[i], live, norm_q, &kqv);
+            if (u == 0) sm.kq[pb][t] = kqv;
+        }
+    }
+    if (w == 0) {
+        const int tl = lane & 31;
+        const bool live = tl < lc;
+        const float gv = bf(pf.gate);
+        const float lg = (lane < 32 && live) ? log2_(fmaxf(gv, 1e-30f)) : 0.f;
+        const float gs = scan32(lg);
+        const float gC = lane_val(gs, C - 1);
+        if (lane < 32) {
+            sm.gl[pb][lane] = gs;
+            sm.eg[pb][lane] = exp2_(gs);
+            sm.ws[pb][lane] = exp2_(gC - gs);
+        } else {
+            sm.be[pb][tl] = live ? gv : 0.f;
+        }
+        if (lane == 0) sm.gC[pb] = gC;
+    }
+}
+
+// ---- key side, part 2 (wave 0): T diag(beta) -> fp16, transposed --------------
+__device__ __forceinline__ void key_side_T(Smem &sm, int pb, int lane) {
+    const _Float16 *kb = sm.kh[pb];
+    const int c = lane & 15, rb = 4 * (lane >> 4);
+    half8 f0[4], f1[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        f0[ks] = ld8(kb + kofs(c, 4 * ks + (lane >> 4), 0));
+        f1[ks] = ld8(kb + kofs(16 + c, 4 * ks + (lane >> 4), 0));
+    }
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    floatx4 G[2] = {z, z}, G01 = z;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        G[0] = mfma16(f0[ks], f0[ks], G[0]);
+        G[1] = mfma16(f1[ks], f1[ks], G[1]);
+        G01 = mfma16(f0[ks], f1[ks], G01);  // (k_r . k_{16+c})
+    }
+    const float *gl = sm.gl[pb];
+    const float *be = sm.be[pb];
+    half4 id4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) id4[j] = (_Float16)(rb + j == c ? 1.f : 0.f);
+
+    floatx4 T00 = z, T11t = z;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        // A (rows > cols) and A^T (rows < cols) of diagonal tile b, split into
+        // the two 8 x 8 diagonal blocks (N) and the lower-left block (L)
+        const float gls = gl[16 * b + c], bes = be[16 * b + c];
+        const float4 glt = *reinterpret_cast<const float4 *>(&gl[16 * b + rb]);
+        const float4 bet = *reinterpret_cast<const float4 *>(&be[16 * b + rb]);
+        const float glv[4] = {glt.x, glt.y, glt.z, glt.w}, bev[4] = {bet.x, bet.y, bet.z, bet.w};
+        floatx4 N, Nt, L, Lt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j;
+            const bool lower = r > c, same8 = ((r ^ c) & 8) == 0;
+            const float d = glv[j] - gls;
+            const float val = r == c ? 0.f : (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * G[b][j];
+            N[j] = (lower && same8) ? val : 0.f;
+            Nt[j] = (!lower && same8) ? val : 0.f;
+            L[j] = (lower && !same8) ? val : 0.f;
+            Lt[j] = (!lower && !same8) ? val : 0.f;
+        }
+        const half4 Nh = h4(N), Nth = h4(Nt), Lh = h4(L), Lth = h4(Lt);
+        const floatx4 N2 = mm16(Nth, Nh, z);     // N N
+        const floatx4 N2t = mm16(Nh, Nth, z);    // N^T N^T
+        const half4 N2h = h4(N2), N2th = h4(N2t);
+        const floatx4 N4t = mm16(N2h, N2th, z);  // (N^2)^T (N^2)^T
+        const floatx4 N4 = mm16(N2th, N2h, z);   // N^2 N^2
+        const floatx4 R1 = mm16(id4 - Nth, id4 + N2h, z);   // (I - N)(I + N^2)
+        const floatx4 R1t = mm16(id4 - Nh, id4 + N2th, z);  // (I - N^T)(I + (N^2)^T)
+        const floatx4 R = mm16(id4 + h4(N4t), h4(R1), z);   // (I + N^4) R1 = blockdiag inverse
+        const floatx4 Rt = mm16(id4 + h4(N4), h4(R1t), z);  // its transpose
+        const half4 Rh = h4(R), Rth = h4(Rt);
+        if (b == 0) {
+            // X = R - R (L R)
+            const floatx4 X = mm16(Lth, Rh, z);
+            T00 = mm16(Rth, -h4(X), R);
+        } else {
+            // X^T = R^T - R^T (L^T R^T)
+            const floatx4 Xt = mm16(Lh, Rth, z);
+            T11t = mm16(Rh, -h4(Xt), Rt);
+        }
+    }
+    // off-diagonal: T_10 = -T_11 A_10 T_00, with A_10^T from the (0, 1) Gram tile
+    floatx4 A10t;
+    {
+        const float gt = gl[16 + c], bt = be[16 + c];
+        const float4 gs4 = *reinterpret_cast<const float4 *>(&gl[rb]);
+        const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A10t[j] = bt * exp2_(gt - gsv[j]) * G01[j];
+    }
+    const floatx4 W = mm16(h4(A10t), h4(T00), z);
+    const floatx4 T10 = mm16(h4(T11t), -h4(W), z);
+
+    // T diag(beta), scaled into the fp16 band, stored as (row s, column t)
+    const float bs0 = be[c];
+    const float4 b14 = *reinterpret_cast<const float4 *>(&be[16 + rb]);
+    const float b1v[4] = {b14.x, b14.y, b14.z, b14.w};
+    floatx4 t00, t10, t11;
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        t00[j] = T00[j] * bs0;
+        t10[j] = T10[j] * bs0;
+        t11[j] = T11t[j] * b1v[j];
+        mx = fmaxf(mx, fmaxf(fabsf(t00[j]), fmaxf(fabsf(t10[j]), fabsf(t11[j]))));
+    }
+    const int eT = f16_adjust(wave_max(mx));
+    if (eT != 0) {
+        const float sc = ldexpf(1.f, eT);
+        t00 *= sc;
+        t10 *= sc;
+        t11 *= sc;
+    }
+    _Float16 *tt = sm.tT[pb];
+    *reinterpret_cast<half4 *>(&tt[c * C + rb]) = h4(t00);        // t = rb + j, s = c
+    *reinterpret_cast<half4 *>(&tt[c * C + 16 + rb]) = h4(t10);   // t = 16 + rb + j, s = c
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tt[(16 + rb + j) * C + 16 + c] = (_Float16)t11[j];  // t = 16 + c, s = 16 + rb + j
+    if (lane == 0) sm.tsc[pb] = ldexpf(1.f, -eT);
+}
+
+// ---- key side, part 3 (wave 1): P -> fp16, transposed -------------------------
+__device__ __forceinline__ void key_side_P(Smem &sm, int pb, int lane) {
+    const _Float16 *kb = sm.kh[pb];
+    const _Float16 *qb = sm.qh[pb];
+    const int c = lane & 15, rb = 4 * (lane >> 4);
+    half8 k0[4], k1[4], q0[4], q1[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int un = 4 * ks + (lane >> 4);
+        k0[ks] = ld8(kb + kofs(c, un, 0));
+        k1[ks] = ld8(kb + kofs(16 + c, un, 0));
+        q0[ks] = ld8(qb + kofs(c, un, 0));
+        q1[ks] = ld8(qb + kofs(16 + c, un, 0));
+    }
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    floatx4 P00 = z, P10 = z, P11 = z;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        P00 = mfma16(q0[ks], k0[ks], P00);
+        P10 = mfma16(q1[ks], k0[ks], P10);
+        P11 = mfma16(q1[ks], k1[ks], P11);
+    }
+    const float *gl = sm.gl[pb];
+    const float g0 = gl[c], g1 = gl[16 + c];
+    const float4 a4 = *reinterpret_cast<const float4 *>(&gl[rb]);
+    const float4 b4 = *reinterpret_cast<const float4 *>(&gl[16 + rb]);
+    const float gt0[4] = {a4.x, a4.y, a4.z, a4.w}, gt1[4] = {b4.x, b4.y, b4.z, b4.w};
+    floatx4 x00, x10, x11;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = rb + j;
+        x00[j] = c <= r ? exp2_(gt0[j] - g0) * P00[j] : 0.f;
+        x10[j] = exp2_(gt1[j] - g0) * P10[j];
+        x11[j] = c <= r ? exp2_(gt1[j] - g1) * P11[j] : 0.f;
+    }
+    _Float16 *pt = sm.pT[pb];
+    *reinterpret_cast<half4 *>(&pt[c * C + rb]) = h4(x00);
+    *reinterpret_cast<half4 *>(&pt[c * C + 16 + rb]) = h4(x10);
+    *reinterpret_cast<half4 *>(&pt[(16 + c) * C + 16 + rb]) = h4(x11);
+}
+
+// ---- state-side operand reads ---------------------------------------------------
+// A fragment (rows t = lane%32, reduction s in the accumulator order of k-step
+// ks) of a matrix stored as (row s, column t) with row stride C.
+__device__ __forceinline__ half8 tr_frag_st(const _Float16 *base, int ks, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+    const int s = 16 * ks + 4 * (g >> 1) + (n >> 2);
+    const int col = 16 * (g & 1) + 4 * (n & 3);
+    return cat(tr4(base + s * C + col), tr4(base + (s + 8) * C + col));
+}
+// A fragment of K^T for state tile a (rows d_k = 32 a + lane%32) and k-step hf.
+__device__ __forceinline__ half8 tr_frag_kt(const _Float16 *kb, int a, int hf, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+    const int t = 16 * hf + 4 * (g >> 1) + (n >> 2);
+    const int s = sqd(n & 3);
+    const int unit = 2 * (2 * a + (g & 1)) + (s >> 1), hh = 4 * (s & 1);
+    return cat(tr4(kb + kofs(t, unit, hh)), tr4(kb + kofs(t + 8, unit, hh)));
+}
+
+// Store S = 2^{-sigma} Sacc (held as S^T tiles) to a d_v x d_k row-major block.
+__device__ __forceinline__ void store_state(float *dst_head, const floatx16 (&Sacc)[4], float sigma, int w,
                                             int l32, int hi32) {
     float *dst = dst_head + (int64_t)(32 * w + l32) * DK;
-    const float sc = ldexpf(1.f, sig);
+    const float sc = exp2_(-sigma);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -255,6 +520,8 @@ __device__ __forceinline__ void store_state(float *dst_head, const floatx16 (&Sa
                 make_float4(Sacc[a][4 * q4] * sc, Sacc[a][4 * q4 + 1] * sc, Sacc[a][4 * q4 + 2] * sc,
                             Sacc[a][4 * q4 + 3] * sc);
 }
+
+__device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
 __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 {
@@ -273,18 +540,15 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     const int dv = 32 * w + l32;
     const bool want_o = P.o != nullptr;
     const bool norm_q = (P.flags & kNormQ) != 0;
-
-    const uint16_t *kg = static_cast<const uint16_t *>(P.k);
-    const uint16_t *qg = static_cast<const uint16_t *>(P.q);
-    const uint16_t *vg = static_cast<const uint16_t *>(P.v);
-    const uint16_t *ag = static_cast<const uint16_t *>(P.alpha);
-    const uint16_t *bg = static_cast<const uint16_t *>(P.beta);
     uint16_t *og = static_cast<uint16_t *>(P.o);
 
-    // ---- state S^T = 2^sig * Sacc: tile a covers d_k rows 32a..32a+31; the
+    const int len = P.len[r];
+    const int64_t row0 = P.row0[r];
+    const int ne_end = P.emit_begin[r + 1];
+
+    // ---- state S^T = 2^{-sigma} Sacc: tile a covers d_k rows 32a..32a+31; the
     // lane holds value row dv and d_k rows 8(j/4) + 4*hi32 + j%4 of each tile.
     floatx16 Sacc[4];
-    int sig = 0;
     if (P.init_off[r] >= 0) {
         const float *src = P.init_base + P.init_off[r] + (int64_t)h * DV * DK + (int64_t)dv * DK;
 #pragma unroll
@@ -303,321 +567,214 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 #pragma unroll
             for (int j = 0; j < 16; ++j) Sacc[a][j] = 0.f;
     }
-
-    // The upper-right 16x16 blocks of P and T are read by the products and
-    // never written.
-    for (int idx = tid; idx < 16 * 16; idx += NT) {
-        sm.pc[(idx >> 4) * TST + 16 + (idx & 15)] = (_Float16)0.f;
-        sm.tc[(idx >> 4) * TST + 16 + (idx & 15)] = (_Float16)0.f;
-    }
-
-    const int len = P.len[r];
-    const int64_t row0 = P.row0[r];
-    int ne = P.emit_begin[r];
-    const int ne_end = P.emit_begin[r + 1];
-    const int lrow = tid >> 4;
-    const int lcol = 8 * (tid & 15);
-
-    int t0 = 0;
-    int lc = len > 0 ? chunk_len(P, len, 0, ne, ne_end) : 0;
-    uint16_t gate = 0;
-    if (len > 0) dma_chunk(sm, gate, kg, qg, vg, ag, bg, row0, H, h, w, lane, lc, want_o);
-
-    while (t0 < len) {
-        vm_lds_barrier();  // staged chunk has landed; the previous chunk's LDS reads are done
-
-        // ---- phase 1: unit keys / queries as fp16 operands, v transposed -------
-#pragma unroll
-        for (int i = 0; i < C / 16; ++i) {
-            const int t = 16 * i + lrow;
-            const bool live = t < lc;
-            const uint4 z4 = make_uint4(0, 0, 0, 0);
-            const uint4 rk = live ? *reinterpret_cast<const uint4 *>(&sm.rk[t * DK + lcol]) : z4;
-            const uint4 rq = (live && want_o) ? *reinterpret_cast<const uint4 *>(&sm.rq[t * DK + lcol]) : z4;
-            const uint4 rv = live ? *reinterpret_cast<const uint4 *>(&sm.rv[t * DV + lcol]) : z4;
-            const uint32_t kw[4] = {rk.x, rk.y, rk.z, rk.w};
-            const uint32_t qw[4] = {rq.x, rq.y, rq.z, rq.w};
-            const uint32_t vw[4] = {rv.x, rv.y, rv.z, rv.w};
-            float kf[8], qf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kf[2 * e] = __uint_as_float(kw[e] << 16);
-                kf[2 * e + 1] = __uint_as_float(kw[e] & 0xffff0000u);
-                qf[2 * e] = __uint_as_float(qw[e] << 16);
-                qf[2 * e + 1] = __uint_as_float(qw[e] & 0xffff0000u);
-            }
-            float kss = 0.f, qss = 0.f, qmx = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kss += kf[e] * kf[e];
-                qss += qf[e] * qf[e];
-                qmx = fmaxf(qmx, fabsf(qf[e]));
-            }
-            kss = row16_sum(kss);  // one token row per 16 lanes
-            qss = row16_sum(qss);
-            if (!norm_q) qmx = row16_max(qmx);
-            // k^ = k / ||k|| (a zero key stays zero); q^ likewise, or q / 2^E
-            const float ks = kss > 0.f ? rsqrtf(kss) : 0.f;
-            int Eq = 0;
-            if (!norm_q) frexpf(qmx, &Eq);
-            const float qs = norm_q ? (qss > 0.f ? rsqrtf(qss) : 0.f) : ldexpf(1.f, -Eq);
-            half8 kh, qh;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kh[e] = (_Float16)(kf[e] * ks);
-                qh[e] = (_Float16)(qf[e] * qs);
-            }
-            _Float16 *kp = &sm.kc[t * KST + lcol];
-            _Float16 *qp = &sm.qc[t * KST + lcol];
-            *reinterpret_cast<half4 *>(kp) = __builtin_shufflevector(kh, kh, 0, 1, 2, 3);
-            *reinterpret_cast<half4 *>(kp + 4) = __builtin_shufflevector(kh, kh, 4, 5, 6, 7);
-            *reinterpret_cast<half4 *>(qp) = __builtin_shufflevector(qh, qh, 0, 1, 2, 3);
-            *reinterpret_cast<half4 *>(qp + 4) = __builtin_shufflevector(qh, qh, 4, 5, 6, 7);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.kct[(lcol + e) * TST + t] = kh[e];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sm.vct[(lcol + 2 * e) * TST + t] = (uint16_t)(vw[e] & 0xffffu);
-                sm.vct[(lcol + 2 * e + 1) * TST + t] = (uint16_t)(vw[e] >> 16);
-            }
-            if ((tid & 15) == 0) sm.kapq[t] = norm_q ? 1.f : ldexpf(1.f, Eq);
-        }
-        if (tid < C) {
-            sm.g[tid] = tid < lc ? log2_(fmaxf(bf(gate), 1e-30f)) : 0.f;
-        } else if (tid >= 64 && tid < 64 + C) {
-            sm.beta[tid - 64] = tid - 64 < lc ? bf(gate) : 0.f;
-        }
-        lds_barrier();
-
-        // ---- phase 2: gate prefix sums and the Gram tiles ----------------------
-        // every wave forms g_t (lane t) itself; wave 0 publishes it for phase 4
-        const float gscan = scan32(lane < C ? sm.g[lane] : 0.f);
-        const float gC = lane_val(gscan, C - 1);
-        const float egC = exp2_(gC);
-        // items: G = K^K^T tiles (0,0), (1,0), (1,1), then Q'K^T tiles; wave w
-        // takes items w and w + 4
-        floatx4 gacc[2];
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int item = w + 4 * it;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (item < 6) {
-                const int idx = item % 3;
-                const int mt = idx > 0 ? 1 : 0, nt = idx == 2 ? 1 : 0;
-                const _Float16 *src = item < 3 ? sm.kc : sm.qc;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int c0 = 32 * ks + 8 * (lane >> 4);
-                    acc = mfma16(frag_contig(src + (16 * mt + (lane & 15)) * KST + c0),
-                                 frag_contig(sm.kc + (16 * nt + (lane & 15)) * KST + c0), acc);
-                }
-            }
-            gacc[it] = acc;
-        }
-        if (w == 0 && lane < C) {
-            sm.eg[lane] = exp2_(gscan);
-            sm.wsc[lane] = exp2_(gC - gscan);
-        }
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int item = w + 4 * it;
-            if (item < 6) {
-                const int idx = item % 3;
-                const int mt = idx > 0 ? 1 : 0, nt = idx == 2 ? 1 : 0;
-                const int s = 16 * nt + (lane & 15);
-                const float gs = __shfl(gscan, s);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * mt + 4 * (lane >> 4) + j;
-                    const float dec = exp2_(__shfl(gscan, t) - gs);
-                    if (item < 3) {
-                        const float a = s < t ? sm.beta[t] * dec * gacc[it][j] : 0.f;
-                        sm.aws[t * AST + s] = a;
-                        if (mt == nt) sm.atd[(16 * mt + (s & 15)) * 16 + (t & 15)] = a;
-                    } else {
-                        sm.pc[t * TST + s] = (_Float16)(s <= t ? dec * gacc[it][j] : 0.f);
-                    }
-                }
-            }
-        }
-        lds_barrier();
-
-        // ---- phase 3 (wave 0): T = (I + A)^{-1} -> fp16 -------------------------
-        if (w == 0) {
-            // diagonal blocks (lanes 0..31: block lane/16, column lane%16) by
-            // column-oriented substitution: once x_s is final, subtract its
-            // multiple from the remaining rows (dependency chain of 16 steps)
-            const int bo = 16 * (lane >> 4), c = lane & 15;
-            float x[16];
-            if (lane < 32) {
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) x[rr] = rr == c ? 1.f : 0.f;
-                const float *at = &sm.atd[bo * 16];
-#pragma unroll
-                for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-                    for (int rr = s2 + 1; rr < 16; ++rr) x[rr] -= at[s2 * 16 + rr] * x[s2];
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) sm.aws[(bo + rr) * AST + bo + c] = x[rr];
-            }
-            // off-diagonal block: T10 = -T11 (A10 T00)
-            const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-            const floatx4 W4 = mfma1616(a1616(sm.aws, AST, 16, 0, lane), b1616(sm.aws, AST, 0, 0, lane), z4);
-            half4 wf;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wf[j] = (_Float16)W4[j];
-            const floatx4 X4 = mfma1616(a1616(sm.aws, AST, 16, 16, lane), wf, z4);
-            // fp16 copy with a power-of-two scale, straight from registers
-            float mx = fmaxf(fmaxf(fabsf(X4[0]), fabsf(X4[1])), fmaxf(fabsf(X4[2]), fabsf(X4[3])));
-            if (lane < 32) {
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, fabsf(x[rr]));
-            }
-            const int eT = fp16_exp(wave_max(mx));
-            const float sc = ldexpf(1.f, eT);
-            if (lane < 32) {
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) sm.tc[(bo + rr) * TST + bo + c] = (_Float16)(x[rr] * sc);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                sm.tc[(16 + 4 * (lane >> 4) + j) * TST + (lane & 15)] = (_Float16)(-X4[j] * sc);
-            if (lane == 0) sm.unT = ldexpf(1.f, -eT);
-        }
-
-        // ---- phase 4a: state-dependent products of wave w ----------------------
-        float smx = 0.f;
+    float sigma = 0.f;  // S = 2^{-sigma} Sacc
+    float mb = 0.f;     // bound on max |Sacc| over this wave
+    if (len > 0) {
+        float mx = 0.f;
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) smx = fmaxf(smx, fabsf(Sacc[a][j]));
-        const int eS = fp16_exp(wave_max(smx));
-        const float scS = ldexpf(1.f, eS);
-        const float unS = ldexpf(1.f, sig - eS);  // S = unS * (fp16 copy)
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(Sacc[a][j]));
+        mx = wave_max(mx);
+        if (mx > 0.f) {
+            int E;
+            frexpf(mx, &E);
+            sigma = (float)(4 - E);
+            const float sc = ldexpf(1.f, 4 - E);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) Sacc[a] *= sc;
+            mb = mx * sc;
+        }
+    }
+
+    // The upper-right 16x16 blocks of T^T and P^T (s >= 16, t < 16) stay zero.
+    for (int idx = tid; idx < 16 * 16; idx += NT) {
+        const int o = (16 + (idx >> 4)) * C + (idx & 15);
+        sm.tT[0][o] = sm.tT[1][o] = (_Float16)0.f;
+        sm.pT[0][o] = sm.pT[1][o] = (_Float16)0.f;
+    }
+
+    Chunk cur;
+    cur.t0 = 0;
+    cur.ne = P.emit_begin[r];
+    cur.lc = len > 0 ? chunk_len(P, len, 0, cur.ne, ne_end) : 0;
+    Chunk nx = next_chunk(P, cur, len, ne_end);
+    Pref pf;
+    int vb = 0;  // V buffer of the current chunk
+    if (cur.lc > 0) {
+        dma_v(sm, 0, P, row0 + cur.t0, cur.lc, H, h, w, lane);
+        if (nx.lc > 0) dma_v(sm, 1, P, row0 + nx.t0, nx.lc, H, h, w, lane);
+        load_kq(pf, P, row0 + cur.t0, cur.lc, H, h, tid, w, lane, want_o);
+    }
+    lds_barrier();
+    if (cur.lc > 0) {
+        key_side_convert(sm, 0, pf, cur.lc, tid, w, lane, want_o, norm_q);
+        if (nx.lc > 0) load_kq(pf, P, row0 + nx.t0, nx.lc, H, h, tid, w, lane, want_o);
+        lds_barrier();
+        if (w == 0) key_side_T(sm, 0, lane);
+        else if (w == 1 && want_o) key_side_P(sm, 0, lane);
+    }
+
+    const int g = lane >> 4, n16 = lane & 15;
+    int p = 0;  // key-side buffer of the current chunk
+    while (cur.lc > 0) {
+        const Chunk nx2 = next_chunk(P, nx, len, ne_end);
+        lds_barrier();  // key side of `cur` complete; previous state step done
+        const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
+        if (nx2.lc > 0) dma_v(sm, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, lane);
+        if (nx.lc > 0) {
+            key_side_convert(sm, p ^ 1, pf, nx.lc, tid, w, lane, want_o, norm_q);
+            if (nx2.lc > 0) load_kq(pf, P, row0 + nx2.t0, nx2.lc, H, h, tid, w, lane, want_o);
+        }
+        lds_barrier();
+        if (nx.lc > 0) {
+            if (w == 0) key_side_T(sm, p ^ 1, lane);
+            else if (w == 1 && want_o) key_side_P(sm, p ^ 1, lane);
+        }
+
+        // ---- state side of `cur` ------------------------------------------------
+        const int lc = cur.lc;
+        const _Float16 *kb = sm.kh[p];
+        const _Float16 *qb = sm.qh[p];
+        float *cw0 = sm.cw[w][0];
+        float *cw1 = sm.cw[w][1];
+        float *cw2 = sm.cw[w][2];
+        float *cw3 = sm.cw[w][3];
+
+        // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
         floatx16 Y = {}, Z = {};
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const half8 sf = to_frag(Sacc[a], ks, scS);
-                Y = mfma32(frag_perm(sm.kc, KST, l32, 32 * a + 16 * ks, lane), sf, Y);
-                if (want_o) Z = mfma32(frag_perm(sm.qc, KST, l32, 32 * a + 16 * ks, lane), sf, Z);
+                const half8 sf = to_frag(Sacc[a], ks);
+                const int un = 2 * (2 * a + ks) + hi32;
+                Y = mfma32(ld8(kb + kofs(l32, un, 0)), sf, Y);
+                if (want_o) Z = mfma32(ld8(qb + kofs(l32, un, 0)), sf, Z);
             }
-        // B_t = beta_t (v_t - 2^{g_t} S0 k^_t), in place in Y
-        float bmx = 0.f;
+        const float isg = exp2_(-sigma);
+        if (lane < 32) {
+            const float e = sm.eg[p][lane];
+            cw0[lane] = e * isg;                   // B~ = v - cw0 Y
+            cw1[lane] = sm.kq[p][lane] * e * isg;  // o (state part) = cw1 Z
+        }
+        // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
+        float bm = 0.f;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int tb = 8 * q4 + 4 * hi32;
-            const uint2 v2 = *reinterpret_cast<const uint2 *>(&sm.vct[dv * TST + tb]);
-            const float4 bt = *reinterpret_cast<const float4 *>(&sm.beta[tb]);
-            const float4 e4 = *reinterpret_cast<const float4 *>(&sm.eg[tb]);
-            const float vv[4] = {__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u),
-                                 __uint_as_float(v2.y << 16), __uint_as_float(v2.y & 0xffff0000u)};
-            const float bb[4] = {bt.x, bt.y, bt.z, bt.w};
-            const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
+            const int t = 8 * q4 + 4 * (g >> 1) + (n16 >> 2);
+            const i16x4_t vv = tr4u(&sm.vr[vb][w][t * 32 + 16 * (g & 1) + 4 * (n16 & 3)]);
+            const float4 c4 = ld4f(&cw0[8 * q4 + 4 * hi32]);
+            const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                const float x = bb[j4] * (vv[j4] - ee[j4] * unS * Y[4 * q4 + j4]);
-                Y[4 * q4 + j4] = x;
-                bmx = fmaxf(bmx, fabsf(x));
+            for (int jj = 0; jj < 4; ++jj) {
+                const float x = bf((uint16_t)vv[jj]) - cc[jj] * Y[4 * q4 + jj];
+                Y[4 * q4 + jj] = x;
+                bm = fmaxf(bm, fabsf(x));
             }
         }
-        const int eB = fp16_exp(wave_max(bmx));
-        const half8 Bf0 = to_frag(Y, 0, ldexpf(1.f, eB));
-        const half8 Bf1 = to_frag(Y, 1, ldexpf(1.f, eB));
-
-        lds_barrier();  // T is ready
-
-        // The staging area was consumed in phase 1: queue the next chunk now so
-        // its copies overlap the rest of this chunk.
-        const int t0n = t0 + lc;
-        int nen = ne;
-        if (nen < ne_end && P.emit_after[nen] == t0n) ++nen;
-        const int lcn = t0n < len ? chunk_len(P, len, t0n, nen, ne_end) : 0;
-        if (lcn > 0) dma_chunk(sm, gate, kg, qg, vg, ag, bg, row0 + t0n, H, h, w, lane, lcn, want_o);
-
-        // ---- phase 4b: U = T B, outputs, state update ---------------------------
+        const int eB = f16_adjust(wave_max(bm));
+        if (eB != 0) Y *= ldexpf(1.f, eB);
+        // U = (T diag(beta)) B~
         floatx16 U = {};
-        U = mfma32(frag_perm(sm.tc, TST, l32, 0, lane), Bf0, U);
-        U = mfma32(frag_perm(sm.tc, TST, l32, 16, lane), Bf1, U);
-        const float unTB = sm.unT * ldexpf(1.f, -eB);
-        float umx = 0.f;
+        U = mfma32(tr_frag_st(sm.tT[p], 0, lane), to_frag(Y, 0), U);
+        U = mfma32(tr_frag_st(sm.tT[p], 1, lane), to_frag(Y, 1), U);
+        float um = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            U[j] *= unTB;
-            umx = fmaxf(umx, fabsf(U[j]));
+        for (int j = 0; j < 16; ++j) um = fmaxf(um, fabsf(U[j]));
+        um = wave_max(um);
+        const float us = sm.tsc[p] * ldexpf(1.f, -eB);  // u = us * U
+        const int eU = f16_adjust(um);
+
+        // scale of the new state: decay folded into sigma; rescale Sacc only
+        // when the bound on max |Sacc| would leave [1, 2^14]
+        float sig1 = sigma - sm.gC[p];
+        const float inc0 = 32.f * um * us * exp2_(sig1);  // |K^T W'| <= 32 max|W'|, max|W'| <= um us 2^sig1
+        float delta = 0.f;
+        if (mb + inc0 > 0x1p14f || (mb + inc0 < 1.f && mb + inc0 > 0.f)) {
+            float mx = 0.f;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(Sacc[a][j]));
+            mx = wave_max(mx);
+            int E;
+            frexpf(mx + inc0, &E);
+            delta = (float)(E - 4);
+            mb = mx;
         }
+        sig1 -= delta;
+        const float dsc = exp2_(-delta);
+        mb = (mb + inc0) * dsc;
+        if (lane < 32) {
+            cw2[lane] = sm.ws[p][lane] * exp2_(sig1) * us;            // W' = cw2 U
+            cw3[lane] = sm.kq[p][lane] * us * ldexpf(1.f, -eU);      // o (intra part) = cw3 (P U')
+        }
+
         if (want_o) {
-            // o_t = kapq_t (2^{g_t} S0 q'_t + sum_s P_ts u_s), staged in this wave's
-            // rows of vct (its v values are consumed) and stored 16 B per lane
-            const int eU = fp16_exp(wave_max(umx));
-            const float scU = ldexpf(1.f, eU), unU = ldexpf(1.f, -eU);
-            floatx16 po = {};
-            po = mfma32(frag_perm(sm.pc, TST, l32, 0, lane), to_frag(U, 0, scU), po);
-            po = mfma32(frag_perm(sm.pc, TST, l32, 16, lane), to_frag(U, 1, scU), po);
-            uint16_t *stage = &sm.vct[32 * w * TST];
+            half8 Uf0 = to_frag(U, 0), Uf1 = to_frag(U, 1);
+            if (eU != 0) {
+                const floatx16 Us = U * ldexpf(1.f, eU);
+                Uf0 = to_frag(Us, 0);
+                Uf1 = to_frag(Us, 1);
+            }
+            floatx16 PO = {};
+            PO = mfma32(tr_frag_st(sm.pT[p], 0, lane), Uf0, PO);
+            PO = mfma32(tr_frag_st(sm.pT[p], 1, lane), Uf1, PO);
+            // o_t, packed as bf16 pairs of neighbouring value columns
+            const bool odd = (l32 & 1) != 0;
+            const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+            uint16_t *orow = og + ((row0 + cur.t0) * H + h) * DV + 32 * w + (l32 & ~1);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int tb = 8 * q4 + 4 * hi32;
-                const float4 e4 = *reinterpret_cast<const float4 *>(&sm.eg[tb]);
-                const float4 k4 = *reinterpret_cast<const float4 *>(&sm.kapq[tb]);
-                const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
-                const float kq[4] = {k4.x, k4.y, k4.z, k4.w};
+                const float4 z4 = ld4f(&cw1[8 * q4 + 4 * hi32]);
+                const float4 p4 = ld4f(&cw3[8 * q4 + 4 * hi32]);
+                const float zz[4] = {z4.x, z4.y, z4.z, z4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
+                float ov[4];
 #pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const float ov = kq[j4] * (ee[j4] * unS * Z[4 * q4 + j4] + unU * po[4 * q4 + j4]);
-                    stage[(tb + j4) * 32 + l32] = __builtin_bit_cast(uint16_t, (__bf16)ov);
-                }
-            }
+                for (int jj = 0; jj < 4; ++jj) ov[jj] = zz[jj] * Z[4 * q4 + jj] + pp[jj] * PO[4 * q4 + jj];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int seg = lane + 64 * m;
-                const int t = seg >> 2, c8 = 8 * (seg & 3);
-                if (t < lc) {
-                    const uint4 o4 = *reinterpret_cast<const uint4 *>(&stage[t * 32 + c8]);
-                    *reinterpret_cast<uint4 *>(og + ((row0 + t0 + t) * H + h) * DV + 32 * w + c8) = o4;
+                for (int pr = 0; pr < 2; ++pr) {
+                    const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ov[2 * pr]) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ov[2 * pr + 1]) << 16);
+                    const uint32_t nb = dppu<0xB1>(pk);
+                    const uint32_t wd = __builtin_amdgcn_perm(nb, pk, sel);
+                    const int tok = 8 * q4 + 4 * hi32 + 2 * pr + (odd ? 1 : 0);
+                    if (tok < lc) *reinterpret_cast<uint32_t *>(orow + (int64_t)tok * H * DV) = wd;
                 }
             }
         }
-        // S_C = 2^{g_C} S0 + sum_s (2^{g_C - g_s} u_s) k^_s^T.  With W = wsc * U
-        // scaled by 2^eW into fp16, the new representation is sig' = -eW:
-        // Sacc' = 2^{g_C} 2^{sig + eW} Sacc + K^T W'.
-        float wmx = 0.f;
+        // W' = 2^{sig1} 2^{g_C - g_s} u_s (Sacc units), then Sacc <- Sacc 2^{-delta} + K^ T W'
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int tb = 8 * q4 + 4 * hi32;
-            const float4 s4 = *reinterpret_cast<const float4 *>(&sm.wsc[tb]);
-            const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                U[4 * q4 + j4] *= ss[j4];
-                wmx = fmaxf(wmx, fabsf(U[4 * q4 + j4]));
-            }
+            const float4 s4 = ld4f(&cw2[8 * q4 + 4 * hi32]);
+            U[4 * q4 + 0] *= s4.x;
+            U[4 * q4 + 1] *= s4.y;
+            U[4 * q4 + 2] *= s4.z;
+            U[4 * q4 + 3] *= s4.w;
         }
-        const int eW = fp16_exp(wave_max(wmx));
-        const float scW = ldexpf(1.f, eW);
-        const half8 Wf0 = to_frag(U, 0, scW);
-        const half8 Wf1 = to_frag(U, 1, scW);
-        const float pre = ldexpf(egC, sig + eW);
+        const half8 Wf0 = to_frag(U, 0), Wf1 = to_frag(U, 1);
+        if (delta != 0.f) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) Sacc[a] *= dsc;
+        }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            floatx16 acc = Sacc[a] * pre;
-            acc = mfma32(frag_perm(sm.kct, TST, 32 * a + l32, 0, lane), Wf0, acc);
-            acc = mfma32(frag_perm(sm.kct, TST, 32 * a + l32, 16, lane), Wf1, acc);
-            Sacc[a] = acc;
+            Sacc[a] = mfma32(tr_frag_kt(kb, a, 0, lane), Wf0, Sacc[a]);
+            Sacc[a] = mfma32(tr_frag_kt(kb, a, 1, lane), Wf1, Sacc[a]);
         }
-        sig = -eW;
+        sigma = sig1;
 
-        t0 += lc;
-        if (ne < ne_end && P.emit_after[ne] == t0) {
-            store_state(P.emit_base + (((int64_t)b * P.M + P.emit_slot[ne]) * H + h) * DV * DK, Sacc,
-                        sig, w, l32, hi32);
-            ++ne;
-        }
-        lc = lcn;
+        if (cur.ne < ne_end && P.emit_after[cur.ne] == cur.t0 + lc)
+            store_state(P.emit_base + (((int64_t)b * P.M + P.emit_slot[cur.ne]) * H + h) * DV * DK, Sacc, sigma,
+                        w, l32, hi32);
+        cur = nx;
+        nx = nx2;
+        p ^= 1;
+        vb = vb == 2 ? 0 : vb + 1;
     }
 
-    store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sig, w, l32, hi32);
+    store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
 }  // namespace
