@@ -101,11 +101,14 @@ def cpu_baseline(w, spans, budget_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel", choices=["auto", "recurrent", "chunked"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-output", action="store_true", help="skip o (state only)")
+    ap.add_argument("--device-warmup-s", type=float, default=0.3,
+                    help="untimed repetitions of the step before the warm-up steps, until the "
+                         "GPU clocks have settled (seconds of wall time)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the replay, time a plain device copy of this many MiB "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -143,6 +146,17 @@ def main():
                         first_pos=w.first_pos, flags=flags, state_out=state, o=o,
                         want_o=o is not None)
 
+    # Device warm-up (untimed): the first ~100 launches run while the GPU clocks
+    # ramp up; repeat the step for a fixed wall-clock interval so that the timed
+    # region measures the steady state, then the W warm-up steps proper.
+    t_dev0 = time.perf_counter()
+    n_dev = 0
+    while time.perf_counter() - t_dev0 < args.device_warmup_s:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        n_dev += 20
+    device_warmup_s = time.perf_counter() - t_dev0
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -205,6 +219,7 @@ def main():
                    "outputs": o is not None, "kernel": "chunked" if chunked else "recurrent"},
         "roofline": roof,
         "wall_s_timed_region": t_wall,
+        "device_warmup": {"seconds": device_warmup_s, "steps": n_dev},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, spans)

@@ -19,13 +19,15 @@
 //
 // Key side (state independent, one chunk ahead of the state chain):
 //  - all waves convert the next chunk's keys/queries to unit fp16 rows;
-//  - wave 0 forms T entirely in registers: the Gram tiles come out of MFMA in
-//    accumulator layout, and because the Gram matrix is symmetric both A and
-//    A^T are available elementwise.  The 8 x 8 diagonal blocks are inverted in
-//    the product form (I + N)^{-1} = (I - N)(I + N^2)(I + N^4) (N^8 = 0), then
-//    two doubling steps X_10 = -X_11 A_10 X_00 give the 16 x 16 and 32 x 32
-//    inverse.  An MFMA A operand of X is X^T in accumulator layout, so X and
-//    X^T are carried side by side where needed;
+//  - T is formed in registers: the Gram tiles come out of MFMA in accumulator
+//    layout, and because the Gram matrix is symmetric both A and A^T are
+//    available elementwise.  In each 16 x 16 diagonal tile (wave 0: tile 0,
+//    wave 2: tile 1) the 8 x 8 diagonal blocks are inverted in the product form
+//    (I + N)^{-1} = (I - N)(I + N^2)(I + N^4) (N^8 = 0), then a doubling step
+//    X_10 = -X_11 A_10 X_00 gives the tile's inverse; wave 3 forms A_10 of the
+//    two tiles and, one barrier later, the last doubling step and the fp16
+//    copy.  An MFMA A operand of X is X^T in accumulator layout, so X and X^T
+//    are carried side by side where needed;
 //  - wave 1 forms P_ts = 2^{g_t - g_s} (q_t . k_s).
 // State side (each wave owns 32 value rows): the state is kept transposed
 // (S^T, d_k x d_v) in v_mfma_f32_32x32x16_f16 accumulator layout, fp32, as
@@ -47,9 +49,15 @@
 // float32.
 //
 // Work split: one workgroup of 4 waves per (request, head), two workgroups per
-// CU (LDS ~68 KB each).  V rows of a chunk are copied into LDS with
+// CU (LDS ~75 KB each).  V rows of a chunk are copied into LDS with
 // global_load_lds_dwordx4 two chunks ahead, each wave copying its own value
-// columns; key/query rows are prefetched into registers one chunk ahead.
+// columns; key/query rows are prefetched into registers one chunk ahead;
+// outputs of a chunk are stored during the next one.
+//
+// Per chunk n, two barriers: after the first, the state chain of n up to B~
+// (which needs no T), the conversion of n + 1 and the last step of T for n;
+// after the second, the tile tasks of n + 1 and the rest of the state chain
+// of n.
 #include "gdn_launch.h"
 #include "gdn_numeric.h"
 
@@ -85,6 +93,7 @@ struct Smem {
     alignas(16) float ws[2][C];          // 2^{g_C - g_t}
     alignas(16) float kq[2][C];          // 1, or 2^{E_t} for unnormalised queries
     alignas(16) float cw[NW][4][C];      // per-wave coefficients (see the state side)
+    alignas(16) float4 tpart[2][3][64];  // T_00, T_11^T, A_10^T tiles (accumulator layout) per lane
     float gC[2];
     float tsc[2];                        // 2^{-eT}
 };
@@ -206,9 +215,8 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 // Lane l copies 16 bytes from base + voff to (LDS base) + 16 l.  Inline
 // assembly with an SGPR base, so that the compiler neither waits for it nor
 // orders LDS accesses of other buffers behind it.
-__device__ __forceinline__ void dma16(uint64_t base, uint32_t voff, void *lds_wave_base) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)lds_wave_base));
+__device__ __forceinline__ void dma16(uint64_t base, uint32_t voff, uint32_t lds_wave_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
@@ -251,7 +259,12 @@ __device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t r
         if (want_q) pf.q[i] = *reinterpret_cast<const uint4 *>(qg + off);
     }
     if (w == 0) {
-        const uint16_t *src = static_cast<const uint16_t *>(lane < 32 ? P.alpha : P.beta);
+        // both base addresses as wave-uniform values first, so that the
+        // per-lane choice is a register select (not a load of the pointer)
+        const uint64_t pa = uniform64(reinterpret_cast<uint64_t>(P.alpha));
+        const uint64_t pbt = uniform64(reinterpret_cast<uint64_t>(P.beta));
+        typedef const __attribute__((address_space(1))) uint16_t gu16;
+        gu16 *src = reinterpret_cast<gu16 *>(lane < 32 ? pa : pbt);
         pf.gate = src[(rowbase + min(lane & 31, lc - 1)) * H + h];
     }
 }
@@ -259,27 +272,29 @@ __device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t r
 // V rows of a chunk into the wave's slice of buffer vb: copy k covers rows
 // 16 k .. 16 k + 15, lane l taking row 16 k + l/4, value columns
 // 32 w + 8 (l%4) .. +7 (LDS: slice + 1 KiB k + 16 l).
-__device__ __forceinline__ void dma_v(Smem &sm, int vb, const LaunchDesc &P, int64_t rowbase, int lc, int H,
-                                      int h, int w, int lane) {
+// sm_lds is the LDS byte address of the workgroup's Smem.
+__device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const LaunchDesc &P, int64_t rowbase, int lc,
+                                      int H, int h, int w, int lane) {
     const uint16_t *vg = static_cast<const uint16_t *>(P.v);
     const uint64_t base = uniform64(reinterpret_cast<uint64_t>(vg + (rowbase * H + h) * DV + 32 * w));
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int row = min(16 * k + (lane >> 2), lc - 1);
         const uint32_t voff = (uint32_t)((row * H * DV + 8 * (lane & 3)) * 2);
-        dma16(base, voff, &sm.vr[vb][w][16 * k * 32]);
+        dma16(base, voff, sm_lds + (uint32_t)offsetof(Smem, vr) + (uint32_t)(((vb * NW + w) * C * 32 + 16 * k * 32) * 2));
     }
 }
 
 // ---- key side, part 1 (all waves): fp16 unit keys / queries and gate sums -----
 __device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 raw, bool live, bool normalise,
                                             float *kq_out) {
+    // rows past the chunk hold a copy of a live row (finite); they get scale 0
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
     float f[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        f[2 * e] = live ? bflo(wd[e]) : 0.f;
-        f[2 * e + 1] = live ? bfhi(wd[e]) : 0.f;
+        f[2 * e] = bflo(wd[e]);
+        f[2 * e + 1] = bfhi(wd[e]);
     }
     float sc;
     if (normalise) {
@@ -287,7 +302,8 @@ __device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 r
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
         ss = row16_sum(ss);  // one token row per 16 lanes
-        sc = ss > 0.f ? rsqrtf(ss) : 0.f;
+        // a key of squared norm below 1e-36 is treated as zero
+        sc = (live && ss > 1e-36f) ? __builtin_amdgcn_rsqf(ss) : 0.f;
     } else {
         float mx = 0.f;
 #pragma unroll
@@ -295,7 +311,7 @@ __device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 r
         mx = row16_max(mx);
         int E = 0;
         frexpf(mx, &E);
-        sc = ldexpf(1.f, -E);
+        sc = live ? ldexpf(1.f, -E) : 0.f;
         if (kq_out) *kq_out = ldexpf(1.f, E);
     }
     half4 lo, hi;
@@ -342,8 +358,65 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
     }
 }
 
-// ---- key side, part 2 (wave 0): T diag(beta) -> fp16, transposed --------------
-__device__ __forceinline__ void key_side_T(Smem &sm, int pb, int lane) {
+// ---- key side, part 2: T = (I + A)^{-1} in three tile tasks and a combine ----
+// Diagonal tile b (tokens 16b .. 16b+15), wave 0 (b = 0) or wave 2 (b = 1):
+// T_bb, returned for b = 0 as T_00 and for b = 1 as T_11^T (both in
+// accumulator layout: lane i holds rows 4(i/16) + j, column i%16).
+__device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, int lane) {
+    const _Float16 *kb = sm.kh[pb];
+    const int c = lane & 15, rb = 4 * (lane >> 4);
+    half8 f[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) f[ks] = ld8(kb + kofs(16 * b + c, 4 * ks + (lane >> 4), 0));
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    floatx4 G = z;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) G = mfma16(f[ks], f[ks], G);
+    const float *gl = sm.gl[pb];
+    const float *be = sm.be[pb];
+    half4 id4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) id4[j] = (_Float16)(rb + j == c ? 1.f : 0.f);
+    // A (rows > cols) and A^T (rows < cols) of the tile, split into the two
+    // 8 x 8 diagonal blocks (N) and the lower-left block (L)
+    const float gls = gl[16 * b + c], bes = be[16 * b + c];
+    const float4 glt = *reinterpret_cast<const float4 *>(&gl[16 * b + rb]);
+    const float4 bet = *reinterpret_cast<const float4 *>(&be[16 * b + rb]);
+    const float glv[4] = {glt.x, glt.y, glt.z, glt.w}, bev[4] = {bet.x, bet.y, bet.z, bet.w};
+    floatx4 N, Nt, L, Lt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = rb + j;
+        const bool lower = r > c, same8 = ((r ^ c) & 8) == 0;
+        const float d = glv[j] - gls;
+        const float val = r == c ? 0.f : (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * G[j];
+        N[j] = (lower && same8) ? val : 0.f;
+        Nt[j] = (!lower && same8) ? val : 0.f;
+        L[j] = (lower && !same8) ? val : 0.f;
+        Lt[j] = (!lower && !same8) ? val : 0.f;
+    }
+    const half4 Nh = h4(N), Nth = h4(Nt), Lh = h4(L), Lth = h4(Lt);
+    const floatx4 N2 = mm16(Nth, Nh, z);     // N N
+    const floatx4 N2t = mm16(Nh, Nth, z);    // N^T N^T
+    const half4 N2h = h4(N2), N2th = h4(N2t);
+    const floatx4 N4t = mm16(N2h, N2th, z);  // (N^2)^T (N^2)^T
+    const floatx4 N4 = mm16(N2th, N2h, z);   // N^2 N^2
+    const floatx4 R1 = mm16(id4 - Nth, id4 + N2h, z);   // (I - N)(I + N^2)
+    const floatx4 R1t = mm16(id4 - Nh, id4 + N2th, z);  // (I - N^T)(I + (N^2)^T)
+    const floatx4 R = mm16(id4 + h4(N4t), h4(R1), z);   // (I + N^4) R1 = blockdiag inverse
+    const floatx4 Rt = mm16(id4 + h4(N4), h4(R1t), z);  // its transpose
+    if (b == 0) {
+        // T_00 = R - R (L R)
+        const floatx4 X = mm16(Lth, h4(R), z);
+        return mm16(h4(Rt), -h4(X), R);
+    }
+    // T_11^T = R^T - R^T (L^T R^T)
+    const floatx4 Xt = mm16(Lh, h4(Rt), z);
+    return mm16(h4(R), -h4(Xt), Rt);
+}
+
+// Wave 3: A_10^T (accumulator layout) from the (0, 1) Gram tile.
+__device__ __forceinline__ floatx4 key_side_a10t(const Smem &sm, int pb, int lane) {
     const _Float16 *kb = sm.kh[pb];
     const int c = lane & 15, rb = 4 * (lane >> 4);
     half8 f0[4], f1[4];
@@ -352,75 +425,29 @@ __device__ __forceinline__ void key_side_T(Smem &sm, int pb, int lane) {
         f0[ks] = ld8(kb + kofs(c, 4 * ks + (lane >> 4), 0));
         f1[ks] = ld8(kb + kofs(16 + c, 4 * ks + (lane >> 4), 0));
     }
-    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-    floatx4 G[2] = {z, z}, G01 = z;
+    floatx4 G01 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        G[0] = mfma16(f0[ks], f0[ks], G[0]);
-        G[1] = mfma16(f1[ks], f1[ks], G[1]);
-        G01 = mfma16(f0[ks], f1[ks], G01);  // (k_r . k_{16+c})
-    }
+    for (int ks = 0; ks < 4; ++ks) G01 = mfma16(f0[ks], f1[ks], G01);  // (k_r . k_{16+c})
     const float *gl = sm.gl[pb];
-    const float *be = sm.be[pb];
-    half4 id4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) id4[j] = (_Float16)(rb + j == c ? 1.f : 0.f);
-
-    floatx4 T00 = z, T11t = z;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        // A (rows > cols) and A^T (rows < cols) of diagonal tile b, split into
-        // the two 8 x 8 diagonal blocks (N) and the lower-left block (L)
-        const float gls = gl[16 * b + c], bes = be[16 * b + c];
-        const float4 glt = *reinterpret_cast<const float4 *>(&gl[16 * b + rb]);
-        const float4 bet = *reinterpret_cast<const float4 *>(&be[16 * b + rb]);
-        const float glv[4] = {glt.x, glt.y, glt.z, glt.w}, bev[4] = {bet.x, bet.y, bet.z, bet.w};
-        floatx4 N, Nt, L, Lt;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = rb + j;
-            const bool lower = r > c, same8 = ((r ^ c) & 8) == 0;
-            const float d = glv[j] - gls;
-            const float val = r == c ? 0.f : (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * G[b][j];
-            N[j] = (lower && same8) ? val : 0.f;
-            Nt[j] = (!lower && same8) ? val : 0.f;
-            L[j] = (lower && !same8) ? val : 0.f;
-            Lt[j] = (!lower && !same8) ? val : 0.f;
-        }
-        const half4 Nh = h4(N), Nth = h4(Nt), Lh = h4(L), Lth = h4(Lt);
-        const floatx4 N2 = mm16(Nth, Nh, z);     // N N
-        const floatx4 N2t = mm16(Nh, Nth, z);    // N^T N^T
-        const half4 N2h = h4(N2), N2th = h4(N2t);
-        const floatx4 N4t = mm16(N2h, N2th, z);  // (N^2)^T (N^2)^T
-        const floatx4 N4 = mm16(N2th, N2h, z);   // N^2 N^2
-        const floatx4 R1 = mm16(id4 - Nth, id4 + N2h, z);   // (I - N)(I + N^2)
-        const floatx4 R1t = mm16(id4 - Nh, id4 + N2th, z);  // (I - N^T)(I + (N^2)^T)
-        const floatx4 R = mm16(id4 + h4(N4t), h4(R1), z);   // (I + N^4) R1 = blockdiag inverse
-        const floatx4 Rt = mm16(id4 + h4(N4), h4(R1t), z);  // its transpose
-        const half4 Rh = h4(R), Rth = h4(Rt);
-        if (b == 0) {
-            // X = R - R (L R)
-            const floatx4 X = mm16(Lth, Rh, z);
-            T00 = mm16(Rth, -h4(X), R);
-        } else {
-            // X^T = R^T - R^T (L^T R^T)
-            const floatx4 Xt = mm16(Lh, Rth, z);
-            T11t = mm16(Rh, -h4(Xt), Rt);
-        }
-    }
-    // off-diagonal: T_10 = -T_11 A_10 T_00, with A_10^T from the (0, 1) Gram tile
+    const float gt = gl[16 + c], bt = sm.be[pb][16 + c];
+    const float4 gs4 = *reinterpret_cast<const float4 *>(&gl[rb]);
+    const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
     floatx4 A10t;
-    {
-        const float gt = gl[16 + c], bt = be[16 + c];
-        const float4 gs4 = *reinterpret_cast<const float4 *>(&gl[rb]);
-        const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) A10t[j] = bt * exp2_(gt - gsv[j]) * G01[j];
-    }
+    for (int j = 0; j < 4; ++j) A10t[j] = bt * exp2_(gt - gsv[j]) * G01[j];
+    return A10t;
+}
+
+// Combine (one wave): T_10 = -T_11 A_10 T_00, then T diag(beta) scaled into
+// the fp16 band and stored as (row s, column t).
+__device__ __forceinline__ void key_side_combine(Smem &sm, int pb, int lane) {
+    const float4 a = sm.tpart[pb][0][lane], bq = sm.tpart[pb][1][lane], cq = sm.tpart[pb][2][lane];
+    const floatx4 T00 = {a.x, a.y, a.z, a.w}, T11t = {bq.x, bq.y, bq.z, bq.w}, A10t = {cq.x, cq.y, cq.z, cq.w};
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
     const floatx4 W = mm16(h4(A10t), h4(T00), z);
     const floatx4 T10 = mm16(h4(T11t), -h4(W), z);
-
-    // T diag(beta), scaled into the fp16 band, stored as (row s, column t)
+    const int c = lane & 15, rb = 4 * (lane >> 4);
+    const float *be = sm.be[pb];
     const float bs0 = be[c];
     const float4 b14 = *reinterpret_cast<const float4 *>(&be[16 + rb]);
     const float b1v[4] = {b14.x, b14.y, b14.z, b14.w};
@@ -446,6 +473,27 @@ __device__ __forceinline__ void key_side_T(Smem &sm, int pb, int lane) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) tt[(16 + rb + j) * C + 16 + c] = (_Float16)t11[j];  // t = 16 + c, s = 16 + rb + j
     if (lane == 0) sm.tsc[pb] = ldexpf(1.f, -eT);
+}
+
+__device__ __forceinline__ void key_side_P(Smem &sm, int pb, int lane);
+
+// Key-side tasks of one chunk after its conversion: wave 0 tile 0, wave 2
+// tile 1, wave 3 A_10^T (kept for the combine), wave 1 P.
+__device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, int lane, bool want_o) {
+    if (w == 1) {
+        if (want_o) key_side_P(sm, pb, lane);
+        return;
+    }
+    floatx4 r;
+    int slot;
+    if (w == 3) {
+        r = key_side_a10t(sm, pb, lane);
+        slot = 2;
+    } else {
+        r = key_side_tile(sm, pb, w >> 1, lane);
+        slot = w >> 1;
+    }
+    sm.tpart[pb][slot][lane] = make_float4(r[0], r[1], r[2], r[3]);
 }
 
 // ---- key side, part 3 (wave 1): P -> fp16, transposed -------------------------
@@ -526,6 +574,7 @@ __device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cas
 __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 {
     __shared__ Smem sm;
+    const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int h = L % P.H;
@@ -602,8 +651,8 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     Pref pf;
     int vb = 0;  // V buffer of the current chunk
     if (cur.lc > 0) {
-        dma_v(sm, 0, P, row0 + cur.t0, cur.lc, H, h, w, lane);
-        if (nx.lc > 0) dma_v(sm, 1, P, row0 + nx.t0, nx.lc, H, h, w, lane);
+        dma_v(sm_lds, 0, P, row0 + cur.t0, cur.lc, H, h, w, lane);
+        if (nx.lc > 0) dma_v(sm_lds, 1, P, row0 + nx.t0, nx.lc, H, h, w, lane);
         load_kq(pf, P, row0 + cur.t0, cur.lc, H, h, tid, w, lane, want_o);
     }
     lds_barrier();
@@ -611,27 +660,22 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         key_side_convert(sm, 0, pf, cur.lc, tid, w, lane, want_o, norm_q);
         if (nx.lc > 0) load_kq(pf, P, row0 + nx.t0, nx.lc, H, h, tid, w, lane, want_o);
         lds_barrier();
-        if (w == 0) key_side_T(sm, 0, lane);
-        else if (w == 1 && want_o) key_side_P(sm, 0, lane);
+        key_side_tasks(sm, 0, w, lane, want_o);
     }
 
     const int g = lane >> 4, n16 = lane & 15;
+    // Outputs of a chunk are stored during the next one, after the loads that
+    // the next chunk waits for have been issued.
+    uint32_t opend[8];
+    uint16_t *orow_pend = og;
+    int lc_pend = 0;
+    const bool odd = (l32 & 1) != 0;
     int p = 0;  // key-side buffer of the current chunk
     while (cur.lc > 0) {
         const Chunk nx2 = next_chunk(P, nx, len, ne_end);
-        lds_barrier();  // key side of `cur` complete; previous state step done
-        const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
-        if (nx2.lc > 0) dma_v(sm, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, lane);
-        if (nx.lc > 0) {
-            key_side_convert(sm, p ^ 1, pf, nx.lc, tid, w, lane, want_o, norm_q);
-            if (nx2.lc > 0) load_kq(pf, P, row0 + nx2.t0, nx2.lc, H, h, tid, w, lane, want_o);
-        }
-        lds_barrier();
-        if (nx.lc > 0) {
-            if (w == 0) key_side_T(sm, p ^ 1, lane);
-            else if (w == 1 && want_o) key_side_P(sm, p ^ 1, lane);
-        }
-
+        lds_barrier();  // key-side tasks of `cur` complete; previous state step done
+        // everything issued before this point (V of the next chunk included) has landed
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         // ---- state side of `cur` ------------------------------------------------
         const int lc = cur.lc;
         const _Float16 *kb = sm.kh[p];
@@ -641,22 +685,41 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         float *cw2 = sm.cw[w][2];
         float *cw3 = sm.cw[w][3];
 
-        // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
+        // Y = K^ Sacc^T (Sacc within the fp16 band by construction)
         floatx16 Y = {}, Z = {};
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const half8 sf = to_frag(Sacc[a], ks);
-                const int un = 2 * (2 * a + ks) + hi32;
-                Y = mfma32(ld8(kb + kofs(l32, un, 0)), sf, Y);
-                if (want_o) Z = mfma32(ld8(qb + kofs(l32, un, 0)), sf, Z);
-            }
+            for (int ks = 0; ks < 2; ++ks)
+                Y = mfma32(ld8(kb + kofs(l32, 2 * (2 * a + ks) + hi32, 0)), to_frag(Sacc[a], ks), Y);
         const float isg = exp2_(-sigma);
         if (lane < 32) {
             const float e = sm.eg[p][lane];
             cw0[lane] = e * isg;                   // B~ = v - cw0 Y
             cw1[lane] = sm.kq[p][lane] * e * isg;  // o (state part) = cw1 Z
+        }
+        // key side of `nx`: conversion (independent of the state chain above)
+        if (nx.lc > 0) key_side_convert(sm, p ^ 1, pf, nx.lc, tid, w, lane, want_o, norm_q);
+        if (nx2.lc > 0) {
+            const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
+            dma_v(sm_lds, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, lane);
+            load_kq(pf, P, row0 + nx2.t0, nx2.lc, H, h, tid, w, lane, want_o);
+        }
+        if (lc_pend > 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int tok = 8 * (k >> 1) + 4 * hi32 + 2 * (k & 1) + (odd ? 1 : 0);
+                if (tok < lc_pend) *reinterpret_cast<uint32_t *>(orow_pend + (int64_t)tok * H * DV) = opend[k];
+            }
+            lc_pend = 0;
+        }
+        // Z = Q^ Sacc^T
+        if (want_o) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    Z = mfma32(ld8(qb + kofs(l32, 2 * (2 * a + ks) + hi32, 0)), to_frag(Sacc[a], ks), Z);
         }
         // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
         float bm = 0.f;
@@ -675,6 +738,10 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         }
         const int eB = f16_adjust(wave_max(bm));
         if (eB != 0) Y *= ldexpf(1.f, eB);
+        if (w == 3) key_side_combine(sm, p, lane);
+        lds_barrier();  // T of `cur` and the keys of `nx` are complete
+        if (nx.lc > 0) key_side_tasks(sm, p ^ 1, w, lane, want_o);
+
         // U = (T diag(beta)) B~
         floatx16 U = {};
         U = mfma32(tr_frag_st(sm.tT[p], 0, lane), to_frag(Y, 0), U);
@@ -721,10 +788,11 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
             floatx16 PO = {};
             PO = mfma32(tr_frag_st(sm.pT[p], 0, lane), Uf0, PO);
             PO = mfma32(tr_frag_st(sm.pT[p], 1, lane), Uf1, PO);
-            // o_t, packed as bf16 pairs of neighbouring value columns
-            const bool odd = (l32 & 1) != 0;
+            // o_t, packed as bf16 pairs of neighbouring value columns: the even
+            // lane keeps token t, the odd lane token t + 1 of each slot pair
             const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-            uint16_t *orow = og + ((row0 + cur.t0) * H + h) * DV + 32 * w + (l32 & ~1);
+            orow_pend = og + ((row0 + cur.t0) * H + h) * DV + 32 * w + (l32 & ~1);
+            lc_pend = lc;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 z4 = ld4f(&cw1[8 * q4 + 4 * hi32]);
@@ -738,9 +806,7 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
                     const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ov[2 * pr]) |
                                         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ov[2 * pr + 1]) << 16);
                     const uint32_t nb = dppu<0xB1>(pk);
-                    const uint32_t wd = __builtin_amdgcn_perm(nb, pk, sel);
-                    const int tok = 8 * q4 + 4 * hi32 + 2 * pr + (odd ? 1 : 0);
-                    if (tok < lc) *reinterpret_cast<uint32_t *>(orow + (int64_t)tok * H * DV) = wd;
+                    opend[2 * q4 + pr] = __builtin_amdgcn_perm(nb, pk, sel);
                 }
             }
         }
@@ -774,6 +840,13 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         vb = vb == 2 ? 0 : vb + 1;
     }
 
+    if (lc_pend > 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tok = 8 * (k >> 1) + 4 * hi32 + 2 * (k & 1) + (odd ? 1 : 0);
+            if (tok < lc_pend) *reinterpret_cast<uint32_t *>(orow_pend + (int64_t)tok * H * DV) = opend[k];
+        }
+    }
     store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
