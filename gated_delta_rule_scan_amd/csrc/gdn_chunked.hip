@@ -156,6 +156,17 @@ __device__ __forceinline__ float scan32(float x) {
     return x;
 }
 
+// Value held by lane l ^ 32.
+__device__ __forceinline__ float partner32(float x, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+// True when the wave maximum of the per-lane maxima m may leave [2^-6, 2^14)
+// (the fp16 band of f16_adjust): some lane at or above 2^14, or all below 2^-6.
+__device__ __forceinline__ bool out_of_band(float m) {
+    return __builtin_amdgcn_ballot_w64(m >= 0x1p14f) != 0 || __builtin_amdgcn_ballot_w64(m >= 0x1p-6f) == 0;
+}
+
 // Power-of-two exponent e for an fp16 operand with maximum magnitude mx: 0 when
 // mx is already in [2^-6, 2^14), else the one bringing mx into [2^7, 2^8).
 __device__ __forceinline__ int f16_adjust(float mx) {
@@ -242,7 +253,7 @@ __device__ __forceinline__ Chunk next_chunk(const LaunchDesc &P, const Chunk &c,
 // ---- loads ---------------------------------------------------------------------
 struct Pref {
     uint4 k[2], q[2];  // raw bf16: rows 16 i + tid/16, columns 8 (tid%16) .. +7
-    uint16_t gate;     // wave 0: alpha (lanes 0..31), beta (lanes 32..63)
+    uint16_t gate;     // wave 1: alpha (lanes 0..31), beta (lanes 32..63)
 };
 
 // Rows past the chunk are clamped to its last row (always in the span), so
@@ -251,21 +262,24 @@ __device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t r
                                         int tid, int w, int lane, bool want_q) {
     const uint16_t *kg = static_cast<const uint16_t *>(P.k);
     const uint16_t *qg = static_cast<const uint16_t *>(P.q);
+    // wave-uniform bases, 32-bit per-lane byte offsets
+    const char *kb = reinterpret_cast<const char *>(kg + (rowbase * H + h) * DK);
+    const char *qb = reinterpret_cast<const char *>(qg + (rowbase * H + h) * DK);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int t = min(16 * i + (tid >> 4), lc - 1);
-        const int64_t off = ((rowbase + t) * H + h) * DK + 8 * (tid & 15);
-        pf.k[i] = *reinterpret_cast<const uint4 *>(kg + off);
-        if (want_q) pf.q[i] = *reinterpret_cast<const uint4 *>(qg + off);
+        const uint32_t off = (uint32_t)(t * H * DK + 8 * (tid & 15)) * 2u;
+        pf.k[i] = *reinterpret_cast<const uint4 *>(kb + off);
+        if (want_q) pf.q[i] = *reinterpret_cast<const uint4 *>(qb + off);
     }
-    if (w == 0) {
+    if (w == 1) {
         // both base addresses as wave-uniform values first, so that the
         // per-lane choice is a register select (not a load of the pointer)
         const uint64_t pa = uniform64(reinterpret_cast<uint64_t>(P.alpha));
         const uint64_t pbt = uniform64(reinterpret_cast<uint64_t>(P.beta));
         typedef const __attribute__((address_space(1))) uint16_t gu16;
-        gu16 *src = reinterpret_cast<gu16 *>(lane < 32 ? pa : pbt);
-        pf.gate = src[(rowbase + min(lane & 31, lc - 1)) * H + h];
+        gu16 *src = reinterpret_cast<gu16 *>(lane < 32 ? pa : pbt) + (rowbase * H + h);
+        pf.gate = src[(uint32_t)(min(lane & 31, lc - 1) * H)];
     }
 }
 
@@ -298,9 +312,13 @@ __device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 r
     }
     float sc;
     if (normalise) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+        for (int e = 0; e < 4; ++e) {
+            const bf16x2 pr = __builtin_bit_cast(bf16x2, wd[e]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+        }
         ss = row16_sum(ss);  // one token row per 16 lanes
         // a key of squared norm below 1e-36 is treated as zero
         sc = (live && ss > 1e-36f) ? __builtin_amdgcn_rsqf(ss) : 0.f;
@@ -340,7 +358,7 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
             if (u == 0) sm.kq[pb][t] = kqv;
         }
     }
-    if (w == 0) {
+    if (w == 1) {
         const int tl = lane & 31;
         const bool live = tl < lc;
         const float gv = bf(pf.gate);
@@ -667,7 +685,7 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     // Outputs of a chunk are stored during the next one, after the loads that
     // the next chunk waits for have been issued.
     uint32_t opend[8];
-    uint16_t *orow_pend = og;
+    char *obase_pend = reinterpret_cast<char *>(og);
     int lc_pend = 0;
     const bool odd = (l32 & 1) != 0;
     int p = 0;  // key-side buffer of the current chunk
@@ -685,19 +703,6 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         float *cw2 = sm.cw[w][2];
         float *cw3 = sm.cw[w][3];
 
-        // Y = K^ Sacc^T (Sacc within the fp16 band by construction)
-        floatx16 Y = {}, Z = {};
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                Y = mfma32(ld8(kb + kofs(l32, 2 * (2 * a + ks) + hi32, 0)), to_frag(Sacc[a], ks), Y);
-        const float isg = exp2_(-sigma);
-        if (lane < 32) {
-            const float e = sm.eg[p][lane];
-            cw0[lane] = e * isg;                   // B~ = v - cw0 Y
-            cw1[lane] = sm.kq[p][lane] * e * isg;  // o (state part) = cw1 Z
-        }
         // key side of `nx`: conversion (independent of the state chain above)
         if (nx.lc > 0) key_side_convert(sm, p ^ 1, pf, nx.lc, tid, w, lane, want_o, norm_q);
         if (nx2.lc > 0) {
@@ -706,20 +711,38 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
             load_kq(pf, P, row0 + nx2.t0, nx2.lc, H, h, tid, w, lane, want_o);
         }
         if (lc_pend > 0) {
+            const uint32_t hdv2 = (uint32_t)(H * DV * 2);
+            const uint32_t lofs = (uint32_t)(4 * hi32 + (odd ? 1 : 0)) * hdv2 + (uint32_t)((l32 & ~1) * 2);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int tok = 8 * (k >> 1) + 4 * hi32 + 2 * (k & 1) + (odd ? 1 : 0);
-                if (tok < lc_pend) *reinterpret_cast<uint32_t *>(orow_pend + (int64_t)tok * H * DV) = opend[k];
+                if (tok < lc_pend)
+                    *reinterpret_cast<uint32_t *>(obase_pend + lofs + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2) =
+                        opend[k];
             }
             lc_pend = 0;
         }
-        // Z = Q^ Sacc^T
-        if (want_o) {
+        // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
+        floatx16 Y = {}, Z = {};
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    Z = mfma32(ld8(qb + kofs(l32, 2 * (2 * a + ks) + hi32, 0)), to_frag(Sacc[a], ks), Z);
+            for (int ks = 0; ks < 2; ++ks) {
+                const half8 sf = to_frag(Sacc[a], ks);
+                const int un = 2 * (2 * a + ks) + hi32;
+                Y = mfma32(ld8(kb + kofs(l32, un, 0)), sf, Y);
+                if (want_o) Z = mfma32(ld8(qb + kofs(l32, un, 0)), sf, Z);
+            }
+        const float isg = exp2_(-sigma);
+        if (lane < 32) {
+            const float e = sm.eg[p][lane];
+            const float kq = sm.kq[p][lane];
+            cw0[lane] = e * isg;       // B~ = v - cw0 Y
+            cw1[lane] = kq * e * isg;  // o (state part) = cw1 Z
+            // W' = cw2 U and o (intra part) = cw3 (P U'), for unscaled T, B~, U
+            // and no rescale of the state (rewritten below otherwise)
+            cw2[lane] = sm.ws[p][lane] * exp2_(sigma - sm.gC[p]);
+            cw3[lane] = kq;
         }
         // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
         float bm = 0.f;
@@ -736,7 +759,8 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
                 bm = fmaxf(bm, fabsf(x));
             }
         }
-        const int eB = f16_adjust(wave_max(bm));
+        int eB = 0;
+        if (out_of_band(bm)) eB = f16_adjust(wave_max(bm));
         if (eB != 0) Y *= ldexpf(1.f, eB);
         if (w == 3) key_side_combine(sm, p, lane);
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
@@ -749,31 +773,37 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         float um = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) um = fmaxf(um, fabsf(U[j]));
-        um = wave_max(um);
-        const float us = sm.tsc[p] * ldexpf(1.f, -eB);  // u = us * U
-        const int eU = f16_adjust(um);
+        int eU = 0;
+        if (out_of_band(um)) eU = f16_adjust(wave_max(um));
+        const float tsc = sm.tsc[p];
+        const float us = tsc * ldexpf(1.f, -eB);  // u = us * U
 
         // scale of the new state: decay folded into sigma; rescale Sacc only
-        // when the bound on max |Sacc| would leave [1, 2^14]
+        // when the bound on max |Sacc| would leave [1, 2^14].  The bound is kept
+        // per value column (lanes l and l ^ 32 hold the column's tokens):
+        // |K^T W'| <= 32 max|W'| and max|W'| <= max|U| us 2^sig1.
         float sig1 = sigma - sm.gC[p];
-        const float inc0 = 32.f * um * us * exp2_(sig1);  // |K^T W'| <= 32 max|W'|, max|W'| <= um us 2^sig1
+        const float incl = 32.f * fmaxf(um, partner32(um, lane)) * us * exp2_(sig1);
+        const float mbn = mb + incl;
         float delta = 0.f;
-        if (mb + inc0 > 0x1p14f || (mb + inc0 < 1.f && mb + inc0 > 0.f)) {
+        if (__builtin_amdgcn_ballot_w64(mbn > 0x1p14f) != 0 ||
+            (__builtin_amdgcn_ballot_w64(mbn >= 1.f) == 0 && __builtin_amdgcn_ballot_w64(mbn > 0.f) != 0)) {
             float mx = 0.f;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(Sacc[a][j]));
-            mx = wave_max(mx);
+            const float tot = wave_max(mx) + wave_max(incl);
             int E;
-            frexpf(mx + inc0, &E);
+            frexpf(tot, &E);
             delta = (float)(E - 4);
-            mb = mx;
+            mb = tot * exp2_(-delta);
+        } else {
+            mb = mbn;
         }
         sig1 -= delta;
         const float dsc = exp2_(-delta);
-        mb = (mb + inc0) * dsc;
-        if (lane < 32) {
+        if ((tsc != 1.f || eB != 0 || eU != 0 || delta != 0.f) && lane < 32) {
             cw2[lane] = sm.ws[p][lane] * exp2_(sig1) * us;            // W' = cw2 U
             cw3[lane] = sm.kq[p][lane] * us * ldexpf(1.f, -eU);      // o (intra part) = cw3 (P U')
         }
@@ -788,19 +818,27 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
             floatx16 PO = {};
             PO = mfma32(tr_frag_st(sm.pT[p], 0, lane), Uf0, PO);
             PO = mfma32(tr_frag_st(sm.pT[p], 1, lane), Uf1, PO);
+            // the intra-chunk part needs no coefficient when q is normalised and
+            // T, B~ and U are unscaled
+            const bool unit_po = norm_q && tsc == 1.f && eB == 0 && eU == 0;
             // o_t, packed as bf16 pairs of neighbouring value columns: the even
             // lane keeps token t, the odd lane token t + 1 of each slot pair
             const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-            orow_pend = og + ((row0 + cur.t0) * H + h) * DV + 32 * w + (l32 & ~1);
+            obase_pend = reinterpret_cast<char *>(og + ((row0 + cur.t0) * H + h) * DV + 32 * w);  // wave-uniform
             lc_pend = lc;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 z4 = ld4f(&cw1[8 * q4 + 4 * hi32]);
-                const float4 p4 = ld4f(&cw3[8 * q4 + 4 * hi32]);
+                const float4 p4 = unit_po ? make_float4(1.f, 1.f, 1.f, 1.f) : ld4f(&cw3[8 * q4 + 4 * hi32]);
                 const float zz[4] = {z4.x, z4.y, z4.z, z4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
                 float ov[4];
+                if (unit_po) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) ov[jj] = zz[jj] * Z[4 * q4 + jj] + pp[jj] * PO[4 * q4 + jj];
+                    for (int jj = 0; jj < 4; ++jj) ov[jj] = zz[jj] * Z[4 * q4 + jj] + PO[4 * q4 + jj];
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) ov[jj] = zz[jj] * Z[4 * q4 + jj] + pp[jj] * PO[4 * q4 + jj];
+                }
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
                     const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ov[2 * pr]) |
@@ -841,10 +879,14 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     }
 
     if (lc_pend > 0) {
+        const uint32_t hdv2 = (uint32_t)(H * DV * 2);
+        const uint32_t lofs = (uint32_t)(4 * hi32 + (odd ? 1 : 0)) * hdv2 + (uint32_t)((l32 & ~1) * 2);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int tok = 8 * (k >> 1) + 4 * hi32 + 2 * (k & 1) + (odd ? 1 : 0);
-            if (tok < lc_pend) *reinterpret_cast<uint32_t *>(orow_pend + (int64_t)tok * H * DV) = opend[k];
+            if (tok < lc_pend)
+                *reinterpret_cast<uint32_t *>(obase_pend + lofs + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2) =
+                    opend[k];
         }
     }
     store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
