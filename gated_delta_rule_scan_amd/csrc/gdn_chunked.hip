@@ -40,8 +40,10 @@
 // T and P as A operands) are read with ds_read_b64_tr_b16 from token-major LDS
 // tiles, so nothing is written transposed.  Keys/queries are stored with the
 // middle two 4-column groups of every 16 columns swapped, so that a lane's
-// 8-element fragment of the permuted reduction order is one 16-byte read, and
-// with the 16-byte units of each row XOR-swizzled against bank conflicts.
+// 8-element fragment of the permuted reduction order is one 16-byte read; their
+// rows are padded to 272 bytes and permuted (krow) so that every read pattern
+// is free of bank conflicts and each lane addresses a tile from one base
+// register plus immediate offsets.
 //
 // Precision: products run on fp16 MFMA with float32 accumulation.  Every fp16
 // operand is kept inside the fp16 normal range by exact power-of-two scales
@@ -68,6 +70,8 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
@@ -80,10 +84,13 @@ constexpr int DV = 128;
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr int NVB = 3;       // V staging buffers (copies run two chunks ahead)
+constexpr int KS = DK + 8;   // key/query tile row stride (halves)
+constexpr int KROWB = 2 * KS;
+constexpr int KBUF = C * KROWB;  // bytes of one key/query tile
 
 struct Smem {
-    alignas(16) _Float16 kh[2][C * DK];  // unit keys, fp16 (layout: kofs)
-    alignas(16) _Float16 qh[2][C * DK];  // q^ (or q / 2^E), fp16 (layout: kofs)
+    alignas(16) _Float16 kh[2][C * KS];  // unit keys, fp16 (layout: krow and the column order below)
+    alignas(16) _Float16 qh[2][C * KS];  // q^ (or q / 2^E), fp16 (same layout)
     alignas(16) uint16_t vr[NVB][NW][C * 32];  // raw bf16 v: [wave][token][32 value columns]
     alignas(16) _Float16 tT[2][C * C];   // (T diag(beta))^T * 2^eT, row s, column t
     alignas(16) _Float16 pT[2][C * C];   // P^T, row s, column t
@@ -97,14 +104,25 @@ struct Smem {
     float gC[2];
     float tsc[2];                        // 2^{-eT}
 };
+constexpr uint32_t OFF_KH = offsetof(Smem, kh);
+constexpr uint32_t OFF_QH = offsetof(Smem, qh);
+constexpr uint32_t OFF_VR = offsetof(Smem, vr);
+constexpr uint32_t OFF_TT = offsetof(Smem, tT);
+constexpr uint32_t OFF_PT = offsetof(Smem, pT);
+constexpr uint32_t OFF_CW = offsetof(Smem, cw);
+static_assert(OFF_QH == OFF_KH + 2 * KBUF, "query tiles follow the key tiles");
 
 // ---- LDS layouts -------------------------------------------------------------
-// kh/qh element (token t, stored column sc): 16-byte unit sc/8 of row t is
-// placed at unit (sc/8) ^ swz(t).  Actual column c is stored at
-// 16 (c/16) + 4 sqd((c/4) % 4) + c % 4 (the middle 4-column groups swapped).
-__device__ __forceinline__ int swz(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
+// Key/query tiles: token t occupies row krow(t) (272 bytes, so row r starts at
+// bank 4 (r mod 16) of the 64 four-byte banks).  Actual column c is stored at
+// 16 (c/16) + 4 sqd((c/4) % 4) + c % 4 (the middle 4-column groups swapped), in
+// 16-byte units u = stored column / 8.  The row order keeps the reads below
+// free of bank conflicts: one unit of 32 consecutive rows (16-byte reads, which
+// the LDS serves in 16-lane groups), four consecutive tokens x 64 bytes
+// (transposed 8-byte reads, served 32 lanes at a time) and 16 rows x units
+// 4g + ks, g = lane / 16 (the tile tasks).
+__device__ __forceinline__ int krow(int t) { return ((4 * (t & 3) + (t >> 2)) & 15) | (t & 16); }
 __device__ __forceinline__ int sqd(int q) { return ((q & 1) << 1) | (q >> 1); }
-__device__ __forceinline__ int kofs(int t, int unit, int h) { return t * DK + ((unit ^ swz(t)) << 3) + h; }
 
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -129,21 +147,24 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += dpp<0x140>(x);  // row_mirror
     return x;
 }
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));
-    x = fmaxf(x, dpp<0x4E>(x));
-    x = fmaxf(x, dpp<0x141>(x));
-    x = fmaxf(x, dpp<0x140>(x));
+// Maxima of non-negative floats as unsigned integers (same order, no NaN
+// canonicalisation), one DPP max per step.
+__device__ __forceinline__ uint32_t row16_umax(uint32_t x) {
+    x = max(x, dppu<0xB1>(x));
+    x = max(x, dppu<0x4E>(x));
+    x = max(x, dppu<0x141>(x));
+    x = max(x, dppu<0x140>(x));
     return x;
 }
+__device__ __forceinline__ float row16_max(float x) { return __uint_as_float(row16_umax(__float_as_uint(x))); }
 __device__ __forceinline__ float lane_val(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 // Maximum over the wave of non-negative values (all lanes active), uniform.
 __device__ __forceinline__ float wave_max(float x) {
-    x = row16_max(x);
-    const uint32_t a = __float_as_uint(lane_val(x, 0)), b = __float_as_uint(lane_val(x, 16));
-    const uint32_t c = __float_as_uint(lane_val(x, 32)), d = __float_as_uint(lane_val(x, 48));
+    const uint32_t m = row16_umax(__float_as_uint(x));
+    const uint32_t a = __builtin_amdgcn_readlane(m, 0), b = __builtin_amdgcn_readlane(m, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(m, 32), d = __builtin_amdgcn_readlane(m, 48);
     return __uint_as_float(max(max(a, b), max(c, d)));
 }
 // Inclusive prefix sum over lanes 0..31 (row_shr within rows, then row_bcast:15).
@@ -179,16 +200,30 @@ __device__ __forceinline__ int f16_adjust(float mx) {
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_to_f32(b); }
 __device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const float2v f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
 
-__device__ __forceinline__ half8 ld8(const _Float16 *p) { return *reinterpret_cast<const half8 *>(p); }
 __device__ __forceinline__ half8 cat(half4 a, half4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
 
+// LDS accesses by byte offset from the workgroup's Smem.
+template <typename T>
+__device__ __forceinline__ T lds_ld(const Smem &sm, uint32_t off) {
+    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(&sm) + off);
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(Smem &sm, uint32_t off, T v) {
+    *reinterpret_cast<T *>(reinterpret_cast<char *>(&sm) + off) = v;
+}
 // 4 halves of a 16-lane transposed read: lane n of each 16-lane group gets
 // element n % 4 of the 8 bytes addressed by lane 4 j + n / 4, for j = 0..3.
-__device__ __forceinline__ half4 tr4(const _Float16 *p) {
+__device__ __forceinline__ half4 tr4(const Smem &sm, uint32_t off) {
+    const char *p = reinterpret_cast<const char *>(&sm) + off;
     return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(p)));
 }
-__device__ __forceinline__ i16x4_t tr4u(const uint16_t *p) {
+__device__ __forceinline__ i16x4_t tr4u(const Smem &sm, uint32_t off) {
+    const char *p = reinterpret_cast<const char *>(&sm) + off;
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
@@ -232,6 +267,62 @@ __device__ __forceinline__ void dma16(uint64_t base, uint32_t voff, uint32_t lds
                  :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
+// ---- per-lane constants ----------------------------------------------------------
+struct Lane {
+    int lane, l32, hi32, g, n16;
+    uint32_t yz;        // Y/Z A fragments: row krow(l32), unit hi32 (+32 bytes per step)
+    uint32_t kt[2][2];  // K^T A fragments: [k-step hf][token + 8]
+    uint32_t task[2];   // tile-task fragments of rows 16 b + lane%16 (+16 bytes per k-step)
+    uint32_t cvt[2];    // conversion stores of rows 16 i + tid/16
+    uint32_t st;        // transposed reads of T^T / P^T
+    uint32_t vrd;       // transposed reads of the wave's V slice
+    uint32_t cwr;       // this wave's coefficient rows, lane half hi32
+    uint32_t ld[2];     // global byte offsets of the key/query rows 16 i + tid/16
+    uint32_t ldc;       // column part of ld (16 bytes per lane of a row)
+    uint32_t vld[2];    // global byte offsets of the V rows 16 k + lane/4
+    uint32_t vldc;
+    uint32_t gld;       // global byte offset of the gate of token lane%32
+    uint32_t ost;       // output store offset (lane pair layout, see the output packing)
+};
+
+__device__ __forceinline__ Lane make_lane(int tid, int w, int H) {
+    Lane L;
+    L.lane = tid & 63;
+    L.l32 = L.lane & 31;
+    L.hi32 = L.lane >> 5;
+    L.g = L.lane >> 4;
+    L.n16 = L.lane & 15;
+    const int g = L.g, n = L.n16;
+    L.yz = krow(L.l32) * KROWB + 16 * L.hi32;
+    {
+        const int s = sqd(n & 3);
+        const uint32_t col = (2 * (g & 1) + (s >> 1)) * 16 + 8 * (s & 1);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int d8 = 0; d8 < 2; ++d8)
+                L.kt[hf][d8] = krow(16 * hf + 4 * (g >> 1) + (n >> 2) + 8 * d8) * KROWB + col;
+    }
+    L.task[0] = krow(n) * KROWB + 64 * g;
+    L.task[1] = krow(16 + n) * KROWB + 64 * g;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) L.cvt[i] = krow(16 * i + 4 * w + g) * KROWB + 32 * (n >> 1) + 8 * (n & 1);
+    L.st = 64 * (4 * (g >> 1) + (n >> 2)) + 2 * (16 * (g & 1) + 4 * (n & 3));
+    L.vrd = 64 * (4 * (g >> 1) + (n >> 2)) + 32 * (g & 1) + 8 * (n & 3);
+    L.cwr = OFF_CW + w * 4 * C * 4 + 16 * L.hi32;
+    const uint32_t hdk2 = (uint32_t)(H * DK * 2);
+    L.ldc = 16 * n;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) L.ld[i] = (uint32_t)(16 * i + 4 * w + g) * hdk2 + L.ldc;
+    L.vldc = 16 * (L.lane & 3);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) L.vld[k] = (uint32_t)(16 * k + (L.lane >> 2)) * hdk2 + L.vldc;
+    L.gld = (uint32_t)(L.l32 * H * 2);
+    const int odd = L.l32 & 1;
+    L.ost = (uint32_t)(4 * L.hi32 + odd) * hdk2 + (uint32_t)((L.l32 & ~1) * 2);
+    return L;
+}
+
 // ---- chunk schedule ------------------------------------------------------------
 struct Chunk {
     int t0, lc, ne;  // first position, length (0: none), first emission not yet taken
@@ -253,33 +344,32 @@ __device__ __forceinline__ Chunk next_chunk(const LaunchDesc &P, const Chunk &c,
 // ---- loads ---------------------------------------------------------------------
 struct Pref {
     uint4 k[2], q[2];  // raw bf16: rows 16 i + tid/16, columns 8 (tid%16) .. +7
-    uint16_t gate;     // wave 1: alpha (lanes 0..31), beta (lanes 32..63)
+    uint16_t ga, gb;   // wave 1: alpha, beta of token lane%32
 };
 
 // Rows past the chunk are clamped to its last row (always in the span), so
 // that every load is issued; their values are ignored by the consumers.
-__device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t rowbase, int lc, int H, int h,
-                                        int tid, int w, int lane, bool want_q) {
-    const uint16_t *kg = static_cast<const uint16_t *>(P.k);
-    const uint16_t *qg = static_cast<const uint16_t *>(P.q);
-    // wave-uniform bases, 32-bit per-lane byte offsets
-    const char *kb = reinterpret_cast<const char *>(kg + (rowbase * H + h) * DK);
-    const char *qb = reinterpret_cast<const char *>(qg + (rowbase * H + h) * DK);
+// row (int64) is the packed row of the chunk's first token.
+template <bool WANT_Q>
+__device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t row, int lc, int H, int h, int w,
+                                        const Lane &L) {
+    const int64_t e0 = (row * H + h) * DK;  // element offset of (row, head)
+    const char *kb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.k) + e0);
+    const char *qb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.q) + e0);
+    const uint32_t lim = (uint32_t)(lc - 1) * (uint32_t)(H * DK * 2) + L.ldc;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int t = min(16 * i + (tid >> 4), lc - 1);
-        const uint32_t off = (uint32_t)(t * H * DK + 8 * (tid & 15)) * 2u;
+        const uint32_t off = min(L.ld[i], lim);
         pf.k[i] = *reinterpret_cast<const uint4 *>(kb + off);
-        if (want_q) pf.q[i] = *reinterpret_cast<const uint4 *>(qb + off);
+        if (WANT_Q) pf.q[i] = *reinterpret_cast<const uint4 *>(qb + off);
     }
     if (w == 1) {
-        // both base addresses as wave-uniform values first, so that the
-        // per-lane choice is a register select (not a load of the pointer)
-        const uint64_t pa = uniform64(reinterpret_cast<uint64_t>(P.alpha));
-        const uint64_t pbt = uniform64(reinterpret_cast<uint64_t>(P.beta));
-        typedef const __attribute__((address_space(1))) uint16_t gu16;
-        gu16 *src = reinterpret_cast<gu16 *>(lane < 32 ? pa : pbt) + (rowbase * H + h);
-        pf.gate = src[(uint32_t)(min(lane & 31, lc - 1) * H)];
+        const int64_t g0 = row * H + h;
+        const char *ab = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.alpha) + g0);
+        const char *bb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.beta) + g0);
+        const uint32_t off = min(L.gld, (uint32_t)((lc - 1) * H * 2));
+        pf.ga = *reinterpret_cast<const uint16_t *>(ab + off);
+        pf.gb = *reinterpret_cast<const uint16_t *>(bb + off);
     }
 }
 
@@ -287,21 +377,21 @@ __device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t r
 // 16 k .. 16 k + 15, lane l taking row 16 k + l/4, value columns
 // 32 w + 8 (l%4) .. +7 (LDS: slice + 1 KiB k + 16 l).
 // sm_lds is the LDS byte address of the workgroup's Smem.
-__device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const LaunchDesc &P, int64_t rowbase, int lc,
-                                      int H, int h, int w, int lane) {
+__device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const LaunchDesc &P, int64_t row, int lc, int H,
+                                      int h, int w, const Lane &L) {
     const uint16_t *vg = static_cast<const uint16_t *>(P.v);
-    const uint64_t base = uniform64(reinterpret_cast<uint64_t>(vg + (rowbase * H + h) * DV + 32 * w));
+    const uint64_t base = uniform64(reinterpret_cast<uint64_t>(vg + (row * H + h) * DV + 32 * w));
+    const uint32_t lim = (uint32_t)(lc - 1) * (uint32_t)(H * DV * 2) + L.vldc;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int row = min(16 * k + (lane >> 2), lc - 1);
-        const uint32_t voff = (uint32_t)((row * H * DV + 8 * (lane & 3)) * 2);
-        dma16(base, voff, sm_lds + (uint32_t)offsetof(Smem, vr) + (uint32_t)(((vb * NW + w) * C * 32 + 16 * k * 32) * 2));
-    }
+    for (int k = 0; k < 2; ++k)
+        dma16(base, min(L.vld[k], lim), sm_lds + OFF_VR + (uint32_t)(((vb * NW + w) * C * 32 + 16 * k * 32) * 2));
 }
 
 // ---- key side, part 1 (all waves): fp16 unit keys / queries and gate sums -----
-__device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 raw, bool live, bool normalise,
-                                            float *kq_out) {
+// Converts the 8 columns of one lane (16-byte unit pair of its row) and stores
+// them at LDS byte offset dst (the row's lower unit; the upper one is +16).
+template <bool NORMALISE>
+__device__ __forceinline__ void convert_row(Smem &sm, uint32_t dst, uint4 raw, bool live, float *kq_out) {
     // rows past the chunk hold a copy of a live row (finite); they get scale 0
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
     float f[8];
@@ -311,12 +401,12 @@ __device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 r
         f[2 * e + 1] = bfhi(wd[e]);
     }
     float sc;
-    if (normalise) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    if (NORMALISE) {
+        typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bf16x2 pr = __builtin_bit_cast(bf16x2, wd[e]);
+            const bf16x2v pr = __builtin_bit_cast(bf16x2v, wd[e]);
             ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
         }
         ss = row16_sum(ss);  // one token row per 16 lanes
@@ -339,53 +429,58 @@ __device__ __forceinline__ void convert_row(_Float16 *dst, int t, int u, uint4 r
         hi[e] = (_Float16)(f[4 + e] * sc);
     }
     // actual 4-column groups 2(u%2), 2(u%2)+1 of 16-group u/2 -> stored groups u%2, 2 + u%2
-    const int g16 = u >> 1, h0 = 4 * (u & 1);
-    *reinterpret_cast<half4 *>(dst + kofs(t, 2 * g16, h0)) = lo;
-    *reinterpret_cast<half4 *>(dst + kofs(t, 2 * g16 + 1, h0)) = hi;
+    lds_st(sm, dst, lo);
+    lds_st(sm, dst + 16, hi);
 }
 
+template <bool WANT_Q, bool NORM_Q>
 __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &pf, int lc, int tid, int w,
-                                                 int lane, bool want_q, bool norm_q) {
-    const int u = tid & 15;
+                                                 const Lane &L) {
+    const uint32_t kbuf = OFF_KH + pb * KBUF, qbuf = OFF_QH + pb * KBUF;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int t = 16 * i + (tid >> 4);
         const bool live = t < lc;
-        convert_row(sm.kh[pb], t, u, pf.k[i], live, true, nullptr);
-        if (want_q) {
+        convert_row<true>(sm, kbuf + L.cvt[i], pf.k[i], live, nullptr);
+        if (WANT_Q) {
             float kqv = 1.f;
-            convert_row(sm.qh[pb], t, u, pf.q[i], live, norm_q, &kqv);
-            if (u == 0) sm.kq[pb][t] = kqv;
+            convert_row<NORM_Q>(sm, qbuf + L.cvt[i], pf.q[i], live, &kqv);
+            if (!NORM_Q && L.n16 == 0) sm.kq[pb][t] = kqv;
         }
     }
     if (w == 1) {
-        const int tl = lane & 31;
+        const int tl = L.l32;
         const bool live = tl < lc;
-        const float gv = bf(pf.gate);
-        const float lg = (lane < 32 && live) ? log2_(fmaxf(gv, 1e-30f)) : 0.f;
+        const float av = bf(pf.ga);
+        const float lg = live ? log2_(fmaxf(av, 1e-30f)) : 0.f;
         const float gs = scan32(lg);
         const float gC = lane_val(gs, C - 1);
-        if (lane < 32) {
-            sm.gl[pb][lane] = gs;
-            sm.eg[pb][lane] = exp2_(gs);
-            sm.ws[pb][lane] = exp2_(gC - gs);
+        if (L.lane < 32) {
+            sm.gl[pb][tl] = gs;
+            sm.eg[pb][tl] = exp2_(gs);
+            sm.ws[pb][tl] = exp2_(gC - gs);
         } else {
-            sm.be[pb][tl] = live ? gv : 0.f;
+            sm.be[pb][tl] = live ? bf(pf.gb) : 0.f;
         }
-        if (lane == 0) sm.gC[pb] = gC;
+        if (L.lane == 0) sm.gC[pb] = gC;
     }
 }
 
 // ---- key side, part 2: T = (I + A)^{-1} in three tile tasks and a combine ----
+// Tile-task operand fragments: rows 16 b + lane%16, k-step ks covering the
+// 16-byte units 4 (lane/16) + ks (the same units on both MFMA operands).
+__device__ __forceinline__ void task_frags(const Smem &sm, uint32_t buf, uint32_t base, half8 (&f)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) f[ks] = lds_ld<half8>(sm, buf + base + 16 * ks);
+}
+
 // Diagonal tile b (tokens 16b .. 16b+15), wave 0 (b = 0) or wave 2 (b = 1):
 // T_bb, returned for b = 0 as T_00 and for b = 1 as T_11^T (both in
 // accumulator layout: lane i holds rows 4(i/16) + j, column i%16).
-__device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, int lane) {
-    const _Float16 *kb = sm.kh[pb];
-    const int c = lane & 15, rb = 4 * (lane >> 4);
+__device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, const Lane &L) {
+    const int c = L.n16, rb = 4 * L.g;
     half8 f[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) f[ks] = ld8(kb + kofs(16 * b + c, 4 * ks + (lane >> 4), 0));
+    task_frags(sm, OFF_KH + pb * KBUF, b ? L.task[1] : L.task[0], f);
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
     floatx4 G = z;
 #pragma unroll
@@ -401,7 +496,7 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
     const float4 glt = *reinterpret_cast<const float4 *>(&gl[16 * b + rb]);
     const float4 bet = *reinterpret_cast<const float4 *>(&be[16 * b + rb]);
     const float glv[4] = {glt.x, glt.y, glt.z, glt.w}, bev[4] = {bet.x, bet.y, bet.z, bet.w};
-    floatx4 N, Nt, L, Lt;
+    floatx4 N, Nt, Lw, Lt;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = rb + j;
@@ -410,10 +505,10 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
         const float val = r == c ? 0.f : (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * G[j];
         N[j] = (lower && same8) ? val : 0.f;
         Nt[j] = (!lower && same8) ? val : 0.f;
-        L[j] = (lower && !same8) ? val : 0.f;
+        Lw[j] = (lower && !same8) ? val : 0.f;
         Lt[j] = (!lower && !same8) ? val : 0.f;
     }
-    const half4 Nh = h4(N), Nth = h4(Nt), Lh = h4(L), Lth = h4(Lt);
+    const half4 Nh = h4(N), Nth = h4(Nt), Lh = h4(Lw), Lth = h4(Lt);
     const floatx4 N2 = mm16(Nth, Nh, z);     // N N
     const floatx4 N2t = mm16(Nh, Nth, z);    // N^T N^T
     const half4 N2h = h4(N2), N2th = h4(N2t);
@@ -434,15 +529,11 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
 }
 
 // Wave 3: A_10^T (accumulator layout) from the (0, 1) Gram tile.
-__device__ __forceinline__ floatx4 key_side_a10t(const Smem &sm, int pb, int lane) {
-    const _Float16 *kb = sm.kh[pb];
-    const int c = lane & 15, rb = 4 * (lane >> 4);
+__device__ __forceinline__ floatx4 key_side_a10t(const Smem &sm, int pb, const Lane &L) {
+    const int c = L.n16, rb = 4 * L.g;
     half8 f0[4], f1[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        f0[ks] = ld8(kb + kofs(c, 4 * ks + (lane >> 4), 0));
-        f1[ks] = ld8(kb + kofs(16 + c, 4 * ks + (lane >> 4), 0));
-    }
+    task_frags(sm, OFF_KH + pb * KBUF, L.task[0], f0);
+    task_frags(sm, OFF_KH + pb * KBUF, L.task[1], f1);
     floatx4 G01 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) G01 = mfma16(f0[ks], f1[ks], G01);  // (k_r . k_{16+c})
@@ -458,13 +549,14 @@ __device__ __forceinline__ floatx4 key_side_a10t(const Smem &sm, int pb, int lan
 
 // Combine (one wave): T_10 = -T_11 A_10 T_00, then T diag(beta) scaled into
 // the fp16 band and stored as (row s, column t).
-__device__ __forceinline__ void key_side_combine(Smem &sm, int pb, int lane) {
+__device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L) {
+    const int lane = L.lane;
     const float4 a = sm.tpart[pb][0][lane], bq = sm.tpart[pb][1][lane], cq = sm.tpart[pb][2][lane];
     const floatx4 T00 = {a.x, a.y, a.z, a.w}, T11t = {bq.x, bq.y, bq.z, bq.w}, A10t = {cq.x, cq.y, cq.z, cq.w};
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
     const floatx4 W = mm16(h4(A10t), h4(T00), z);
     const floatx4 T10 = mm16(h4(T11t), -h4(W), z);
-    const int c = lane & 15, rb = 4 * (lane >> 4);
+    const int c = L.n16, rb = 4 * L.g;
     const float *be = sm.be[pb];
     const float bs0 = be[c];
     const float4 b14 = *reinterpret_cast<const float4 *>(&be[16 + rb]);
@@ -493,41 +585,14 @@ __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, int lane) {
     if (lane == 0) sm.tsc[pb] = ldexpf(1.f, -eT);
 }
 
-__device__ __forceinline__ void key_side_P(Smem &sm, int pb, int lane);
-
-// Key-side tasks of one chunk after its conversion: wave 0 tile 0, wave 2
-// tile 1, wave 3 A_10^T (kept for the combine), wave 1 P.
-__device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, int lane, bool want_o) {
-    if (w == 1) {
-        if (want_o) key_side_P(sm, pb, lane);
-        return;
-    }
-    floatx4 r;
-    int slot;
-    if (w == 3) {
-        r = key_side_a10t(sm, pb, lane);
-        slot = 2;
-    } else {
-        r = key_side_tile(sm, pb, w >> 1, lane);
-        slot = w >> 1;
-    }
-    sm.tpart[pb][slot][lane] = make_float4(r[0], r[1], r[2], r[3]);
-}
-
 // ---- key side, part 3 (wave 1): P -> fp16, transposed -------------------------
-__device__ __forceinline__ void key_side_P(Smem &sm, int pb, int lane) {
-    const _Float16 *kb = sm.kh[pb];
-    const _Float16 *qb = sm.qh[pb];
-    const int c = lane & 15, rb = 4 * (lane >> 4);
+__device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
+    const int c = L.n16, rb = 4 * L.g;
     half8 k0[4], k1[4], q0[4], q1[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int un = 4 * ks + (lane >> 4);
-        k0[ks] = ld8(kb + kofs(c, un, 0));
-        k1[ks] = ld8(kb + kofs(16 + c, un, 0));
-        q0[ks] = ld8(qb + kofs(c, un, 0));
-        q1[ks] = ld8(qb + kofs(16 + c, un, 0));
-    }
+    task_frags(sm, OFF_KH + pb * KBUF, L.task[0], k0);
+    task_frags(sm, OFF_KH + pb * KBUF, L.task[1], k1);
+    task_frags(sm, OFF_QH + pb * KBUF, L.task[0], q0);
+    task_frags(sm, OFF_QH + pb * KBUF, L.task[1], q1);
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
     floatx4 P00 = z, P10 = z, P11 = z;
 #pragma unroll
@@ -555,22 +620,36 @@ __device__ __forceinline__ void key_side_P(Smem &sm, int pb, int lane) {
     *reinterpret_cast<half4 *>(&pt[(16 + c) * C + 16 + rb]) = h4(x11);
 }
 
+// Key-side tasks of one chunk after its conversion: wave 0 tile 0, wave 2
+// tile 1, wave 3 A_10^T (kept for the combine), wave 1 P.
+template <bool WANT_O>
+__device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, const Lane &L) {
+    if (w == 1) {
+        if (WANT_O) key_side_P(sm, pb, L);
+        return;
+    }
+    floatx4 r;
+    int slot;
+    if (w == 3) {
+        r = key_side_a10t(sm, pb, L);
+        slot = 2;
+    } else {
+        r = key_side_tile(sm, pb, w >> 1, L);
+        slot = w >> 1;
+    }
+    sm.tpart[pb][slot][L.lane] = make_float4(r[0], r[1], r[2], r[3]);
+}
+
 // ---- state-side operand reads ---------------------------------------------------
 // A fragment (rows t = lane%32, reduction s in the accumulator order of k-step
-// ks) of a matrix stored as (row s, column t) with row stride C.
-__device__ __forceinline__ half8 tr_frag_st(const _Float16 *base, int ks, int lane) {
-    const int g = lane >> 4, n = lane & 15;
-    const int s = 16 * ks + 4 * (g >> 1) + (n >> 2);
-    const int col = 16 * (g & 1) + 4 * (n & 3);
-    return cat(tr4(base + s * C + col), tr4(base + (s + 8) * C + col));
+// ks) of a 32 x 32 fp16 matrix stored as (row s, column t) at LDS offset mat.
+__device__ __forceinline__ half8 tr_frag_st(const Smem &sm, uint32_t mat, int ks, const Lane &L) {
+    const uint32_t o = mat + L.st + 1024 * ks;
+    return cat(tr4(sm, o), tr4(sm, o + 512));
 }
 // A fragment of K^T for state tile a (rows d_k = 32 a + lane%32) and k-step hf.
-__device__ __forceinline__ half8 tr_frag_kt(const _Float16 *kb, int a, int hf, int lane) {
-    const int g = lane >> 4, n = lane & 15;
-    const int t = 16 * hf + 4 * (g >> 1) + (n >> 2);
-    const int s = sqd(n & 3);
-    const int unit = 2 * (2 * a + (g & 1)) + (s >> 1), hh = 4 * (s & 1);
-    return cat(tr4(kb + kofs(t, unit, hh)), tr4(kb + kofs(t + 8, unit, hh)));
+__device__ __forceinline__ half8 tr_frag_kt(const Smem &sm, uint32_t kbuf, int a, int hf, const Lane &L) {
+    return cat(tr4(sm, kbuf + L.kt[hf][0] + 64 * a), tr4(sm, kbuf + L.kt[hf][1] + 64 * a));
 }
 
 // Store S = 2^{-sigma} Sacc (held as S^T tiles) to a d_v x d_k row-major block.
@@ -587,27 +666,45 @@ __device__ __forceinline__ void store_state(float *dst_head, const floatx16 (&Sa
                             Sacc[a][4 * q4 + 3] * sc);
 }
 
-__device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+// Outputs of one chunk (bf16 pairs of neighbouring value columns, see the
+// output packing) to the rows starting at obase; tokens at or past lc are
+// skipped.
+__device__ __forceinline__ void store_o(char *obase, const uint32_t (&opend)[8], int lc, uint32_t hdv2,
+                                        const Lane &L) {
+    const int odd = L.l32 & 1;
+    if (lc == C) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<uint32_t *>(obase + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2 + L.ost) = opend[k];
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tok = 8 * (k >> 1) + 4 * L.hi32 + 2 * (k & 1) + odd;
+            if (tok < lc)
+                *reinterpret_cast<uint32_t *>(obase + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2 + L.ost) =
+                    opend[k];
+        }
+    }
+}
 
+template <bool WANT_O, bool NORM_Q>
 __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 {
     __shared__ Smem sm;
     const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = L % P.H;
-    const int r = L / P.H;
+    const int Lg = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = Lg % P.H;
+    const int r = Lg / P.H;
     const int b = P.req[r];
     const int H = P.H;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int hi32 = lane >> 5;
+    const Lane L = make_lane(tid, w, H);
+    const int lane = L.lane, l32 = L.l32, hi32 = L.hi32;
     const int dv = 32 * w + l32;
-    const bool want_o = P.o != nullptr;
-    const bool norm_q = (P.flags & kNormQ) != 0;
     uint16_t *og = static_cast<uint16_t *>(P.o);
+    const uint32_t hdv2 = (uint32_t)(H * DV * 2);
 
     const int len = P.len[r];
     const int64_t row0 = P.row0[r];
@@ -635,7 +732,7 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
             for (int j = 0; j < 16; ++j) Sacc[a][j] = 0.f;
     }
     float sigma = 0.f;  // S = 2^{-sigma} Sacc
-    float mb = 0.f;     // bound on max |Sacc| over this wave
+    float mb = 0.f;     // bound on max |Sacc| per value column (lanes l, l ^ 32)
     if (len > 0) {
         float mx = 0.f;
 #pragma unroll
@@ -669,19 +766,18 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     Pref pf;
     int vb = 0;  // V buffer of the current chunk
     if (cur.lc > 0) {
-        dma_v(sm_lds, 0, P, row0 + cur.t0, cur.lc, H, h, w, lane);
-        if (nx.lc > 0) dma_v(sm_lds, 1, P, row0 + nx.t0, nx.lc, H, h, w, lane);
-        load_kq(pf, P, row0 + cur.t0, cur.lc, H, h, tid, w, lane, want_o);
+        dma_v(sm_lds, 0, P, row0 + cur.t0, cur.lc, H, h, w, L);
+        if (nx.lc > 0) dma_v(sm_lds, 1, P, row0 + nx.t0, nx.lc, H, h, w, L);
+        load_kq<WANT_O>(pf, P, row0 + cur.t0, cur.lc, H, h, w, L);
     }
     lds_barrier();
     if (cur.lc > 0) {
-        key_side_convert(sm, 0, pf, cur.lc, tid, w, lane, want_o, norm_q);
-        if (nx.lc > 0) load_kq(pf, P, row0 + nx.t0, nx.lc, H, h, tid, w, lane, want_o);
+        key_side_convert<WANT_O, NORM_Q>(sm, 0, pf, cur.lc, tid, w, L);
+        if (nx.lc > 0) load_kq<WANT_O>(pf, P, row0 + nx.t0, nx.lc, H, h, w, L);
         lds_barrier();
-        key_side_tasks(sm, 0, w, lane, want_o);
+        key_side_tasks<WANT_O>(sm, 0, w, L);
     }
 
-    const int g = lane >> 4, n16 = lane & 15;
     // Outputs of a chunk are stored during the next one, after the loads that
     // the next chunk waits for have been issued.
     uint32_t opend[8];
@@ -696,30 +792,19 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         // ---- state side of `cur` ------------------------------------------------
         const int lc = cur.lc;
-        const _Float16 *kb = sm.kh[p];
-        const _Float16 *qb = sm.qh[p];
-        float *cw0 = sm.cw[w][0];
-        float *cw1 = sm.cw[w][1];
-        float *cw2 = sm.cw[w][2];
-        float *cw3 = sm.cw[w][3];
+        const uint32_t kbuf = OFF_KH + p * KBUF;  // keys of `cur`; queries at + 2 KBUF
+        const uint32_t cw = L.cwr;                 // cw[w][j][8 q4 + 4 hi32 ..] at cw + 128 j + 32 q4
+        float *cwl = sm.cw[w][0];
 
         // key side of `nx`: conversion (independent of the state chain above)
-        if (nx.lc > 0) key_side_convert(sm, p ^ 1, pf, nx.lc, tid, w, lane, want_o, norm_q);
+        if (nx.lc > 0) key_side_convert<WANT_O, NORM_Q>(sm, p ^ 1, pf, nx.lc, tid, w, L);
         if (nx2.lc > 0) {
             const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
-            dma_v(sm_lds, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, lane);
-            load_kq(pf, P, row0 + nx2.t0, nx2.lc, H, h, tid, w, lane, want_o);
+            dma_v(sm_lds, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
+            load_kq<WANT_O>(pf, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
         }
-        if (lc_pend > 0) {
-            const uint32_t hdv2 = (uint32_t)(H * DV * 2);
-            const uint32_t lofs = (uint32_t)(4 * hi32 + (odd ? 1 : 0)) * hdv2 + (uint32_t)((l32 & ~1) * 2);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int tok = 8 * (k >> 1) + 4 * hi32 + 2 * (k & 1) + (odd ? 1 : 0);
-                if (tok < lc_pend)
-                    *reinterpret_cast<uint32_t *>(obase_pend + lofs + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2) =
-                        opend[k];
-            }
+        if (WANT_O && lc_pend > 0) {
+            store_o(obase_pend, opend, lc_pend, hdv2, L);
             lc_pend = 0;
         }
         // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
@@ -729,47 +814,55 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const half8 sf = to_frag(Sacc[a], ks);
-                const int un = 2 * (2 * a + ks) + hi32;
-                Y = mfma32(ld8(kb + kofs(l32, un, 0)), sf, Y);
-                if (want_o) Z = mfma32(ld8(qb + kofs(l32, un, 0)), sf, Z);
+                const uint32_t o = kbuf + L.yz + 32 * (2 * a + ks);
+                Y = mfma32(lds_ld<half8>(sm, o), sf, Y);
+                if (WANT_O) Z = mfma32(lds_ld<half8>(sm, o + 2 * KBUF), sf, Z);
             }
         const float isg = exp2_(-sigma);
         if (lane < 32) {
             const float e = sm.eg[p][lane];
-            const float kq = sm.kq[p][lane];
-            cw0[lane] = e * isg;       // B~ = v - cw0 Y
-            cw1[lane] = kq * e * isg;  // o (state part) = cw1 Z
+            const float kq = NORM_Q ? 1.f : sm.kq[p][lane];
+            cwl[lane] = e * isg;                 // B~ = v - cw0 Y
+            if (WANT_O) cwl[C + lane] = kq * e * isg;  // o (state part) = cw1 Z
             // W' = cw2 U and o (intra part) = cw3 (P U'), for unscaled T, B~, U
             // and no rescale of the state (rewritten below otherwise)
-            cw2[lane] = sm.ws[p][lane] * exp2_(sigma - sm.gC[p]);
-            cw3[lane] = kq;
+            cwl[2 * C + lane] = sm.ws[p][lane] * exp2_(sigma - sm.gC[p]);
+            if (WANT_O && !NORM_Q) cwl[3 * C + lane] = kq;
         }
         // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
         float bm = 0.f;
+        {
+            const uint32_t vbase = OFF_VR + (uint32_t)((vb * NW + w) * C * 32 * 2) + L.vrd;
+            i16x4_t vv[4];
+            float4 c4[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int t = 8 * q4 + 4 * (g >> 1) + (n16 >> 2);
-            const i16x4_t vv = tr4u(&sm.vr[vb][w][t * 32 + 16 * (g & 1) + 4 * (n16 & 3)]);
-            const float4 c4 = ld4f(&cw0[8 * q4 + 4 * hi32]);
-            const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+            for (int q4 = 0; q4 < 4; ++q4) {
+                vv[q4] = tr4u(sm, vbase + 512 * q4);
+                c4[q4] = lds_ld<float4>(sm, cw + 32 * q4);
+            }
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float x = bf((uint16_t)vv[jj]) - cc[jj] * Y[4 * q4 + jj];
-                Y[4 * q4 + jj] = x;
-                bm = fmaxf(bm, fabsf(x));
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float cc[4] = {c4[q4].x, c4[q4].y, c4[q4].z, c4[q4].w};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float x = bf((uint16_t)vv[q4][jj]) - cc[jj] * Y[4 * q4 + jj];
+                    Y[4 * q4 + jj] = x;
+                    bm = fmaxf(bm, fabsf(x));
+                }
             }
         }
         int eB = 0;
         if (out_of_band(bm)) eB = f16_adjust(wave_max(bm));
         if (eB != 0) Y *= ldexpf(1.f, eB);
-        if (w == 3) key_side_combine(sm, p, lane);
+        if (w == 3) key_side_combine(sm, p, L);
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
-        if (nx.lc > 0) key_side_tasks(sm, p ^ 1, w, lane, want_o);
+        if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
 
         // U = (T diag(beta)) B~
+        const uint32_t tmat = OFF_TT + p * (C * C * 2);
         floatx16 U = {};
-        U = mfma32(tr_frag_st(sm.tT[p], 0, lane), to_frag(Y, 0), U);
-        U = mfma32(tr_frag_st(sm.tT[p], 1, lane), to_frag(Y, 1), U);
+        U = mfma32(tr_frag_st(sm, tmat, 0, L), to_frag(Y, 0), U);
+        U = mfma32(tr_frag_st(sm, tmat, 1, L), to_frag(Y, 1), U);
         float um = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) um = fmaxf(um, fabsf(U[j]));
@@ -803,55 +896,61 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         }
         sig1 -= delta;
         const float dsc = exp2_(-delta);
-        if ((tsc != 1.f || eB != 0 || eU != 0 || delta != 0.f) && lane < 32) {
-            cw2[lane] = sm.ws[p][lane] * exp2_(sig1) * us;            // W' = cw2 U
-            cw3[lane] = sm.kq[p][lane] * us * ldexpf(1.f, -eU);      // o (intra part) = cw3 (P U')
+        const bool scaled = tsc != 1.f || eB != 0 || eU != 0 || delta != 0.f;
+        if (scaled && lane < 32) {
+            cwl[2 * C + lane] = sm.ws[p][lane] * exp2_(sig1) * us;  // W' = cw2 U
+            if (WANT_O) cwl[3 * C + lane] = (NORM_Q ? 1.f : sm.kq[p][lane]) * us * ldexpf(1.f, -eU);  // o (intra) = cw3 (P U')
         }
 
-        if (want_o) {
+        if (WANT_O) {
             half8 Uf0 = to_frag(U, 0), Uf1 = to_frag(U, 1);
             if (eU != 0) {
                 const floatx16 Us = U * ldexpf(1.f, eU);
                 Uf0 = to_frag(Us, 0);
                 Uf1 = to_frag(Us, 1);
             }
+            const uint32_t pmat = OFF_PT + p * (C * C * 2);
             floatx16 PO = {};
-            PO = mfma32(tr_frag_st(sm.pT[p], 0, lane), Uf0, PO);
-            PO = mfma32(tr_frag_st(sm.pT[p], 1, lane), Uf1, PO);
-            // the intra-chunk part needs no coefficient when q is normalised and
-            // T, B~ and U are unscaled
-            const bool unit_po = norm_q && tsc == 1.f && eB == 0 && eU == 0;
+            PO = mfma32(tr_frag_st(sm, pmat, 0, L), Uf0, PO);
+            PO = mfma32(tr_frag_st(sm, pmat, 1, L), Uf1, PO);
             // o_t, packed as bf16 pairs of neighbouring value columns: the even
             // lane keeps token t, the odd lane token t + 1 of each slot pair
             const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
             obase_pend = reinterpret_cast<char *>(og + ((row0 + cur.t0) * H + h) * DV + 32 * w);  // wave-uniform
             lc_pend = lc;
+            float ov[16];
+            // the intra-chunk part needs no coefficient when q is normalised and
+            // T, B~ and U are unscaled
+            if (NORM_Q && !scaled) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 z4 = ld4f(&cw1[8 * q4 + 4 * hi32]);
-                const float4 p4 = unit_po ? make_float4(1.f, 1.f, 1.f, 1.f) : ld4f(&cw3[8 * q4 + 4 * hi32]);
-                const float zz[4] = {z4.x, z4.y, z4.z, z4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
-                float ov[4];
-                if (unit_po) {
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 z4 = lds_ld<float4>(sm, cw + 128 + 32 * q4);
+                    const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) ov[jj] = zz[jj] * Z[4 * q4 + jj] + PO[4 * q4 + jj];
-                } else {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) ov[jj] = zz[jj] * Z[4 * q4 + jj] + pp[jj] * PO[4 * q4 + jj];
+                    for (int jj = 0; jj < 4; ++jj) ov[4 * q4 + jj] = zz[jj] * Z[4 * q4 + jj] + PO[4 * q4 + jj];
                 }
+            } else {
 #pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ov[2 * pr]) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ov[2 * pr + 1]) << 16);
-                    const uint32_t nb = dppu<0xB1>(pk);
-                    opend[2 * q4 + pr] = __builtin_amdgcn_perm(nb, pk, sel);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 z4 = lds_ld<float4>(sm, cw + 128 + 32 * q4);
+                    const float4 p4 = lds_ld<float4>(sm, cw + 384 + 32 * q4);
+                    const float zz[4] = {z4.x, z4.y, z4.z, z4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        ov[4 * q4 + jj] = zz[jj] * Z[4 * q4 + jj] + pp[jj] * PO[4 * q4 + jj];
                 }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t pk = pack_bf16(ov[2 * k], ov[2 * k + 1]);
+                const uint32_t nb = dppu<0xB1>(pk);
+                opend[k] = __builtin_amdgcn_perm(nb, pk, sel);
             }
         }
         // W' = 2^{sig1} 2^{g_C - g_s} u_s (Sacc units), then Sacc <- Sacc 2^{-delta} + K^ T W'
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 s4 = ld4f(&cw2[8 * q4 + 4 * hi32]);
+            const float4 s4 = lds_ld<float4>(sm, cw + 256 + 32 * q4);
             U[4 * q4 + 0] *= s4.x;
             U[4 * q4 + 1] *= s4.y;
             U[4 * q4 + 2] *= s4.z;
@@ -864,8 +963,8 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            Sacc[a] = mfma32(tr_frag_kt(kb, a, 0, lane), Wf0, Sacc[a]);
-            Sacc[a] = mfma32(tr_frag_kt(kb, a, 1, lane), Wf1, Sacc[a]);
+            Sacc[a] = mfma32(tr_frag_kt(sm, kbuf, a, 0, L), Wf0, Sacc[a]);
+            Sacc[a] = mfma32(tr_frag_kt(sm, kbuf, a, 1, L), Wf1, Sacc[a]);
         }
         sigma = sig1;
 
@@ -878,17 +977,7 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         vb = vb == 2 ? 0 : vb + 1;
     }
 
-    if (lc_pend > 0) {
-        const uint32_t hdv2 = (uint32_t)(H * DV * 2);
-        const uint32_t lofs = (uint32_t)(4 * hi32 + (odd ? 1 : 0)) * hdv2 + (uint32_t)((l32 & ~1) * 2);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int tok = 8 * (k >> 1) + 4 * hi32 + 2 * (k & 1) + (odd ? 1 : 0);
-            if (tok < lc_pend)
-                *reinterpret_cast<uint32_t *>(obase_pend + lofs + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2) =
-                    opend[k];
-        }
-    }
+    if (WANT_O && lc_pend > 0) store_o(obase_pend, opend, lc_pend, hdv2, L);
     store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
@@ -902,7 +991,15 @@ hipError_t launch_chunked(const LaunchDesc &d, int dk, int dv, Elem e, hipStream
     if (!chunked_supported(dk, dv, e)) return hipErrorNotSupported;
     const int nwg = d.nreq * d.H;
     if (nwg == 0) return hipSuccess;
-    hipLaunchKernelGGL(chunked_kernel, dim3(nwg), dim3(NT), 0, s, d);
+    const bool want_o = d.o != nullptr, norm_q = (d.flags & kNormQ) != 0;
+    if (want_o && norm_q)
+        hipLaunchKernelGGL((chunked_kernel<true, true>), dim3(nwg), dim3(NT), 0, s, d);
+    else if (want_o)
+        hipLaunchKernelGGL((chunked_kernel<true, false>), dim3(nwg), dim3(NT), 0, s, d);
+    else if (norm_q)
+        hipLaunchKernelGGL((chunked_kernel<false, true>), dim3(nwg), dim3(NT), 0, s, d);
+    else
+        hipLaunchKernelGGL((chunked_kernel<false, false>), dim3(nwg), dim3(NT), 0, s, d);
     return hipGetLastError();
 }
 
