@@ -128,6 +128,10 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Keeps the compiler from moving memory accesses across this point (LDS
+// reads above it stay issued early); no wait is implied.
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -282,8 +286,17 @@ struct Lane {
     uint32_t vld[2];    // global byte offsets of the V rows 16 k + lane/4
     uint32_t vldc;
     uint32_t gld;       // global byte offset of the gate of token lane%32
-    uint32_t ost;       // output store offset (lane pair layout, see the output packing)
+    uint32_t ow[4];     // output staging: stores of tokens 8 q4 + 4 hi32 .. +3 of column lane%32
+    uint32_t orr[2][2]; // output staging: transposed reads [token half k][column half]
+    uint32_t ost;       // output row offset: token lane%16 (+16 k), columns 8 (lane/16) .. +7
 };
+
+// Output staging tile of one wave (32 value columns x 32 tokens, bf16, in the
+// wave's V slice once B~ has consumed it): column c holds 8 slots of 4
+// consecutive tokens, slot s at byte 64 c + 8 (s ^ ostg(c)).  The swizzle keeps
+// both the 8-byte stores (32 columns, one slot) and the transposed reads that
+// turn it back into token rows free of bank conflicts.
+__device__ __forceinline__ int ostg(int c) { return (((c >> 3) & 1) << 2) | (((c >> 4) & 1) << 1) | ((c >> 2) & 1); }
 
 __device__ __forceinline__ Lane make_lane(int tid, int w, int H) {
     Lane L;
@@ -318,8 +331,18 @@ __device__ __forceinline__ Lane make_lane(int tid, int w, int H) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) L.vld[k] = (uint32_t)(16 * k + (L.lane >> 2)) * hdk2 + L.vldc;
     L.gld = (uint32_t)(L.l32 * H * 2);
-    const int odd = L.l32 & 1;
-    L.ost = (uint32_t)(4 * L.hi32 + odd) * hdk2 + (uint32_t)((L.l32 & ~1) * 2);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) L.ow[q4] = 64 * L.l32 + 8 * ((2 * q4 + L.hi32) ^ ostg(L.l32));
+    // transposed read k, h: lane (g, n) supplies slot 4 k + n%4 of column 8 g + n/4 + 4 h, so that it
+    // receives token 16 k + n, columns 8 g + 4 h .. +3
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int c = 8 * g + (n >> 2) + 4 * hh;
+            L.orr[k][hh] = 64 * c + 8 * ((4 * k + (n & 3)) ^ ostg(c));
+        }
+    L.ost = (uint32_t)n * hdk2 + 16 * g;
     return L;
 }
 
@@ -666,27 +689,6 @@ __device__ __forceinline__ void store_state(float *dst_head, const floatx16 (&Sa
                             Sacc[a][4 * q4 + 3] * sc);
 }
 
-// Outputs of one chunk (bf16 pairs of neighbouring value columns, see the
-// output packing) to the rows starting at obase; tokens at or past lc are
-// skipped.
-__device__ __forceinline__ void store_o(char *obase, const uint32_t (&opend)[8], int lc, uint32_t hdv2,
-                                        const Lane &L) {
-    const int odd = L.l32 & 1;
-    if (lc == C) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<uint32_t *>(obase + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2 + L.ost) = opend[k];
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int tok = 8 * (k >> 1) + 4 * L.hi32 + 2 * (k & 1) + odd;
-            if (tok < lc)
-                *reinterpret_cast<uint32_t *>(obase + (uint32_t)(8 * (k >> 1) + 2 * (k & 1)) * hdv2 + L.ost) =
-                    opend[k];
-        }
-    }
-}
-
 template <bool WANT_O, bool NORM_Q>
 __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 {
@@ -778,18 +780,17 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         key_side_tasks<WANT_O>(sm, 0, w, L);
     }
 
-    // Outputs of a chunk are stored during the next one, after the loads that
-    // the next chunk waits for have been issued.
-    uint32_t opend[8];
-    char *obase_pend = reinterpret_cast<char *>(og);
-    int lc_pend = 0;
-    const bool odd = (l32 & 1) != 0;
-    int p = 0;  // key-side buffer of the current chunk
+    int p = 0;         // key-side buffer of the current chunk
+    bool tail2 = false;  // the last two vector-memory operations issued are output stores
     while (cur.lc > 0) {
         const Chunk nx2 = next_chunk(P, nx, len, ne_end);
         lds_barrier();  // key-side tasks of `cur` complete; previous state step done
-        // everything issued before this point (V of the next chunk included) has landed
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+        // every load issued before this point has landed (outputs of the previous
+        // chunk, the last two operations when tail2 is set, may still be in flight)
+        if (WANT_O && tail2)
+            __builtin_amdgcn_s_waitcnt(0x0F72);
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         // ---- state side of `cur` ------------------------------------------------
         const int lc = cur.lc;
         const uint32_t kbuf = OFF_KH + p * KBUF;  // keys of `cur`; queries at + 2 KBUF
@@ -798,26 +799,29 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 
         // key side of `nx`: conversion (independent of the state chain above)
         if (nx.lc > 0) key_side_convert<WANT_O, NORM_Q>(sm, p ^ 1, pf, nx.lc, tid, w, L);
-        if (nx2.lc > 0) {
-            const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
-            dma_v(sm_lds, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
-            load_kq<WANT_O>(pf, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
-        }
-        if (WANT_O && lc_pend > 0) {
-            store_o(obase_pend, opend, lc_pend, hdv2, L);
-            lc_pend = 0;
-        }
         // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
+        // (all fragments are read first, so that the reads overlap)
+        half8 kf[8], qf[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            kf[m] = lds_ld<half8>(sm, kbuf + L.yz + 32 * m);
+            if (WANT_O) qf[m] = lds_ld<half8>(sm, kbuf + 2 * KBUF + L.yz + 32 * m);
+        }
         floatx16 Y = {}, Z = {};
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int m = 0; m < 8; ++m) {
+            const half8 sf = to_frag(Sacc[m >> 1], m & 1);
+            Y = mfma32(kf[m], sf, Y);
+            if (WANT_O) Z = mfma32(qf[m], sf, Z);
+        }
+        // schedule: all reads, then per step the fragment conversion and the products
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const half8 sf = to_frag(Sacc[a], ks);
-                const uint32_t o = kbuf + L.yz + 32 * (2 * a + ks);
-                Y = mfma32(lds_ld<half8>(sm, o), sf, Y);
-                if (WANT_O) Z = mfma32(lds_ld<half8>(sm, o + 2 * KBUF), sf, Z);
-            }
+        for (int i = 0; i < (WANT_O ? 16 : 8); ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, WANT_O ? 2 : 1, 0);
+        }
         const float isg = exp2_(-sigma);
         if (lane < 32) {
             const float e = sm.eg[p][lane];
@@ -856,26 +860,46 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         if (eB != 0) Y *= ldexpf(1.f, eB);
         if (w == 3) key_side_combine(sm, p, L);
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
+        // operands of `cur` that are complete now are read before the tasks
+        const half8 tfr0 = tr_frag_st(sm, OFF_TT + p * (C * C * 2), 0, L);
+        const half8 tfr1 = tr_frag_st(sm, OFF_TT + p * (C * C * 2), 1, L);
+        half8 pfr0, pfr1;
+        if (WANT_O) {
+            pfr0 = tr_frag_st(sm, OFF_PT + p * (C * C * 2), 0, L);
+            pfr1 = tr_frag_st(sm, OFF_PT + p * (C * C * 2), 1, L);
+        }
+        const float tsc = sm.tsc[p];
+        const float gCp = sm.gC[p];
         if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
+        // loads of `nx2` (V copies first: their count is fixed, see the wait above)
+        if (nx2.lc > 0) {
+            const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
+            dma_v(sm_lds, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
+            load_kq<WANT_O>(pf, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
+        }
 
         // U = (T diag(beta)) B~
-        const uint32_t tmat = OFF_TT + p * (C * C * 2);
         floatx16 U = {};
-        U = mfma32(tr_frag_st(sm, tmat, 0, L), to_frag(Y, 0), U);
-        U = mfma32(tr_frag_st(sm, tmat, 1, L), to_frag(Y, 1), U);
+        U = mfma32(tfr0, to_frag(Y, 0), U);
+        U = mfma32(tfr1, to_frag(Y, 1), U);
+        // K^T fragments of the state update
+        half8 ktf[4][2];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) ktf[a][hf] = tr_frag_kt(sm, kbuf, a, hf, L);
         float um = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) um = fmaxf(um, fabsf(U[j]));
         int eU = 0;
         if (out_of_band(um)) eU = f16_adjust(wave_max(um));
-        const float tsc = sm.tsc[p];
         const float us = tsc * ldexpf(1.f, -eB);  // u = us * U
 
         // scale of the new state: decay folded into sigma; rescale Sacc only
         // when the bound on max |Sacc| would leave [1, 2^14].  The bound is kept
         // per value column (lanes l and l ^ 32 hold the column's tokens):
         // |K^T W'| <= 32 max|W'| and max|W'| <= max|U| us 2^sig1.
-        float sig1 = sigma - sm.gC[p];
+        float sig1 = sigma - gCp;
         const float incl = 32.f * fmaxf(um, partner32(um, lane)) * us * exp2_(sig1);
         const float mbn = mb + incl;
         float delta = 0.f;
@@ -909,15 +933,9 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
                 Uf0 = to_frag(Us, 0);
                 Uf1 = to_frag(Us, 1);
             }
-            const uint32_t pmat = OFF_PT + p * (C * C * 2);
             floatx16 PO = {};
-            PO = mfma32(tr_frag_st(sm, pmat, 0, L), Uf0, PO);
-            PO = mfma32(tr_frag_st(sm, pmat, 1, L), Uf1, PO);
-            // o_t, packed as bf16 pairs of neighbouring value columns: the even
-            // lane keeps token t, the odd lane token t + 1 of each slot pair
-            const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-            obase_pend = reinterpret_cast<char *>(og + ((row0 + cur.t0) * H + h) * DV + 32 * w);  // wave-uniform
-            lc_pend = lc;
+            PO = mfma32(pfr0, Uf0, PO);
+            PO = mfma32(pfr1, Uf1, PO);
             float ov[16];
             // the intra-chunk part needs no coefficient when q is normalised and
             // T, B~ and U are unscaled
@@ -940,12 +958,38 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
                         ov[4 * q4 + jj] = zz[jj] * Z[4 * q4 + jj] + pp[jj] * PO[4 * q4 + jj];
                 }
             }
+            // o_t to token rows through the wave's V slice (B~ has consumed it),
+            // then two 16-byte stores per lane
+            const uint32_t vsl = OFF_VR + (uint32_t)((vb * NW + w) * C * 32 * 2);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t pk = pack_bf16(ov[2 * k], ov[2 * k + 1]);
-                const uint32_t nb = dppu<0xB1>(pk);
-                opend[k] = __builtin_amdgcn_perm(nb, pk, sel);
+            for (int q4 = 0; q4 < 4; ++q4)
+                lds_st(sm, vsl + L.ow[q4],
+                       make_uint2(pack_bf16(ov[4 * q4], ov[4 * q4 + 1]), pack_bf16(ov[4 * q4 + 2], ov[4 * q4 + 3])));
+            uint4 orow[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const i16x4_t lo = tr4u(sm, vsl + L.orr[k][0]), hi = tr4u(sm, vsl + L.orr[k][1]);
+                orow[k] = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
+            char *ob = reinterpret_cast<char *>(og + ((row0 + cur.t0) * H + h) * DV + 32 * w);  // wave-uniform
+            // a fresh 32-bit lane offset, so that the stores take the uniform base
+            // in SGPRs (not a 64-bit address per lane)
+            uint32_t ost = L.ost;
+            asm volatile("" : "+v"(ost));
+            if (lc == C) {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    char *obk = ob + (size_t)(16 * k) * hdv2;
+                    *reinterpret_cast<uint4 *>(obk + ost) = orow[k];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    char *obk = ob + (size_t)(16 * k) * hdv2;
+                    if (16 * k + L.n16 < lc) *reinterpret_cast<uint4 *>(obk + ost) = orow[k];
+                }
+            }
+            tail2 = lc == C;
         }
         // W' = 2^{sig1} 2^{g_C - g_s} u_s (Sacc units), then Sacc <- Sacc 2^{-delta} + K^ T W'
 #pragma unroll
@@ -963,8 +1007,8 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            Sacc[a] = mfma32(tr_frag_kt(sm, kbuf, a, 0, L), Wf0, Sacc[a]);
-            Sacc[a] = mfma32(tr_frag_kt(sm, kbuf, a, 1, L), Wf1, Sacc[a]);
+            Sacc[a] = mfma32(ktf[a][0], Wf0, Sacc[a]);
+            Sacc[a] = mfma32(ktf[a][1], Wf1, Sacc[a]);
         }
         sigma = sig1;
 
@@ -977,7 +1021,6 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         vb = vb == 2 ? 0 : vb + 1;
     }
 
-    if (WANT_O && lc_pend > 0) store_o(obase_pend, opend, lc_pend, hdv2, L);
     store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
