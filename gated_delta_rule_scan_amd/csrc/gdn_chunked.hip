@@ -83,7 +83,7 @@ constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;
-constexpr int NVB = 3;       // V staging buffers (copies run two chunks ahead)
+constexpr int NVB = 2;       // V staging buffers (copies run one chunk ahead)
 constexpr int KS = DK + 8;   // key/query tile row stride (halves)
 constexpr int KROWB = 2 * KS;
 constexpr int KBUF = C * KROWB;  // bytes of one key/query tile
@@ -91,8 +91,9 @@ constexpr int KBUF = C * KROWB;  // bytes of one key/query tile
 struct Smem {
     alignas(16) _Float16 kh[2][C * KS];  // unit keys, fp16 (layout: krow and the column order below)
     alignas(16) _Float16 qh[2][C * KS];  // q^ (or q / 2^E), fp16 (same layout)
+    alignas(16) uint16_t kqr[2][C * DK];  // raw bf16 keys, queries of the chunk after next: [token][column]
     alignas(16) uint16_t vr[NVB][NW][C * 32];  // raw bf16 v: [wave][token][32 value columns]
-    alignas(16) _Float16 tT[2][C * C];   // (T diag(beta))^T * 2^eT, row s, column t
+    alignas(16) _Float16 tT[C * C];      // (T diag(beta))^T * 2^eT, row s, column t
     alignas(16) _Float16 pT[2][C * C];   // P^T, row s, column t
     alignas(16) float gl[2][C];          // chunk-local prefix sum of log2 alpha
     alignas(16) float be[2][C];          // beta (0 past the chunk)
@@ -100,13 +101,14 @@ struct Smem {
     alignas(16) float ws[2][C];          // 2^{g_C - g_t}
     alignas(16) float kq[2][C];          // 1, or 2^{E_t} for unnormalised queries
     alignas(16) float cw[NW][4][C];      // per-wave coefficients (see the state side)
-    alignas(16) float4 tpart[2][3][64];  // T_00, T_11^T, A_10^T tiles (accumulator layout) per lane
+    alignas(16) float4 tpart[3][64];     // T_00, T_11^T, A_10^T tiles (accumulator layout) per lane
     float gC[2];
-    float tsc[2];                        // 2^{-eT}
+    float tsc;                           // 2^{-eT}
 };
 constexpr uint32_t OFF_KH = offsetof(Smem, kh);
 constexpr uint32_t OFF_QH = offsetof(Smem, qh);
 constexpr uint32_t OFF_VR = offsetof(Smem, vr);
+constexpr uint32_t OFF_KQR = offsetof(Smem, kqr);
 constexpr uint32_t OFF_TT = offsetof(Smem, tT);
 constexpr uint32_t OFF_PT = offsetof(Smem, pT);
 constexpr uint32_t OFF_CW = offsetof(Smem, cw);
@@ -281,22 +283,27 @@ struct Lane {
     uint32_t st;        // transposed reads of T^T / P^T
     uint32_t vrd;       // transposed reads of the wave's V slice
     uint32_t cwr;       // this wave's coefficient rows, lane half hi32
-    uint32_t ld[2];     // global byte offsets of the key/query rows 16 i + tid/16
+    uint32_t ld[2];     // global byte offsets of the key/query rows 8 w + 4 j + lane/16 (copy j)
     uint32_t ldc;       // column part of ld (16 bytes per lane of a row)
     uint32_t vld[2];    // global byte offsets of the V rows 16 k + lane/4
     uint32_t vldc;
     uint32_t gld;       // global byte offset of the gate of token lane%32
-    uint32_t ow[4];     // output staging: stores of tokens 8 q4 + 4 hi32 .. +3 of column lane%32
-    uint32_t orr[2][2]; // output staging: transposed reads [token half k][column half]
-    uint32_t ost;       // output row offset: token lane%16 (+16 k), columns 8 (lane/16) .. +7
+    uint32_t ow[4];     // output staging: stores of tokens 8 q4 + 4 hi32 .. +3 of column 32 w + lane%32
+    uint32_t orr[2][2]; // output staging: transposed reads [row group k][column half]
+    uint32_t ost;       // output store offset: row (lane%16)%4 (+ 8 w + 4 k), columns 32 (lane/16) + 8 ((lane%16)/4) .. +7
 };
 
-// Output staging tile of one wave (32 value columns x 32 tokens, bf16, in the
-// wave's V slice once B~ has consumed it): column c holds 8 slots of 4
-// consecutive tokens, slot s at byte 64 c + 8 (s ^ ostg(c)).  The swizzle keeps
-// both the 8-byte stores (32 columns, one slot) and the transposed reads that
-// turn it back into token rows free of bank conflicts.
+// Output staging tile of a chunk (32 tokens x 128 value columns, bf16, in the
+// chunk's V buffer once every wave's B~ has consumed it): wave w's columns
+// 32 w + c hold 8 slots of 4 consecutive tokens each, slot s at byte
+// 2048 w + 64 c + 8 (s ^ ostg(c) ^ (w & 1)).  The swizzle keeps the 8-byte
+// stores (one slot of 32 columns) and the transposed reads that rebuild full
+// token rows (one slot of 16 columns from each of two waves per 32 lanes) free
+// of bank conflicts.
 __device__ __forceinline__ int ostg(int c) { return (((c >> 3) & 1) << 2) | (((c >> 4) & 1) << 1) | ((c >> 2) & 1); }
+__device__ __forceinline__ uint32_t ostage(int w, int c, int slot) {
+    return 2048 * w + 64 * c + 8 * (slot ^ ostg(c) ^ (w & 1));
+}
 
 __device__ __forceinline__ Lane make_lane(int tid, int w, int H) {
     Lane L;
@@ -326,23 +333,21 @@ __device__ __forceinline__ Lane make_lane(int tid, int w, int H) {
     const uint32_t hdk2 = (uint32_t)(H * DK * 2);
     L.ldc = 16 * n;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) L.ld[i] = (uint32_t)(16 * i + 4 * w + g) * hdk2 + L.ldc;
+    for (int j = 0; j < 2; ++j) L.ld[j] = (uint32_t)(8 * w + 4 * j + g) * hdk2 + L.ldc;
     L.vldc = 16 * (L.lane & 3);
 #pragma unroll
     for (int k = 0; k < 2; ++k) L.vld[k] = (uint32_t)(16 * k + (L.lane >> 2)) * hdk2 + L.vldc;
     L.gld = (uint32_t)(L.l32 * H * 2);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) L.ow[q4] = 64 * L.l32 + 8 * ((2 * q4 + L.hi32) ^ ostg(L.l32));
-    // transposed read k, h: lane (g, n) supplies slot 4 k + n%4 of column 8 g + n/4 + 4 h, so that it
-    // receives token 16 k + n, columns 8 g + 4 h .. +3
+    for (int q4 = 0; q4 < 4; ++q4) L.ow[q4] = ostage(w, L.l32, 2 * q4 + L.hi32);
+    // transposed read (k, hh) of the rows 8 w + 4 k .. +3 (slot 2 w + k): lane (g, n) supplies the
+    // slot of column 8 (n%4) + n/4 + 4 hh of wave g's part, so that it receives token
+    // 8 w + 4 k + n%4, columns 32 g + 8 (n/4) + 4 hh .. +3
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int c = 8 * g + (n >> 2) + 4 * hh;
-            L.orr[k][hh] = 64 * c + 8 * ((4 * k + (n & 3)) ^ ostg(c));
-        }
-    L.ost = (uint32_t)n * hdk2 + 16 * g;
+        for (int hh = 0; hh < 2; ++hh) L.orr[k][hh] = ostage(g, 8 * (n & 3) + (n >> 2) + 4 * hh, 2 * w + k);
+    L.ost = (uint32_t)(n & 3) * hdk2 + 64 * g + 16 * (n >> 2);
     return L;
 }
 
@@ -366,27 +371,28 @@ __device__ __forceinline__ Chunk next_chunk(const LaunchDesc &P, const Chunk &c,
 
 // ---- loads ---------------------------------------------------------------------
 struct Pref {
-    uint4 k[2], q[2];  // raw bf16: rows 16 i + tid/16, columns 8 (tid%16) .. +7
     uint16_t ga, gb;   // wave 1: alpha, beta of token lane%32
 };
 
-// Rows past the chunk are clamped to its last row (always in the span), so
-// that every load is issued; their values are ignored by the consumers.
-// row (int64) is the packed row of the chunk's first token.
-template <bool WANT_Q>
-__device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t row, int lc, int H, int h, int w,
-                                        const Lane &L) {
+// Keys (and queries) of a chunk into the raw tiles: wave w copies rows
+// 8 w .. 8 w + 7, 1 KiB (4 rows) per copy, lane l taking row 8 w + 4 j + l/16,
+// columns 8 (l%16) .. +7.  Rows past the chunk are clamped to its last row
+// (always in the span), so that every copy is issued; their values are ignored
+// by the consumers.  The gates (wave 1) go to registers.  row (int64) is the
+// packed row of the chunk's first token.
+// WHICH = 0: keys; 1: queries (when COPY) and, from wave 1, the gates.
+template <int WHICH, bool COPY = true>
+__device__ __forceinline__ void load_kq(Pref &pf, uint32_t sm_lds, const LaunchDesc &P, int64_t row, int lc, int H,
+                                        int h, int w, const Lane &L) {
     const int64_t e0 = (row * H + h) * DK;  // element offset of (row, head)
-    const char *kb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.k) + e0);
-    const char *qb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.q) + e0);
+    const uint64_t base = uniform64(reinterpret_cast<uint64_t>(static_cast<const uint16_t *>(WHICH ? P.q : P.k) + e0));
     const uint32_t lim = (uint32_t)(lc - 1) * (uint32_t)(H * DK * 2) + L.ldc;
+    if (COPY) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint32_t off = min(L.ld[i], lim);
-        pf.k[i] = *reinterpret_cast<const uint4 *>(kb + off);
-        if (WANT_Q) pf.q[i] = *reinterpret_cast<const uint4 *>(qb + off);
+        for (int j = 0; j < 2; ++j)
+            dma16(base, min(L.ld[j], lim), sm_lds + OFF_KQR + (uint32_t)((WHICH * C + 8 * w + 4 * j) * DK * 2));
     }
-    if (w == 1) {
+    if (WHICH == 1 && w == 1) {
         const int64_t g0 = row * H + h;
         const char *ab = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.alpha) + g0);
         const char *bb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.beta) + g0);
@@ -400,13 +406,14 @@ __device__ __forceinline__ void load_kq(Pref &pf, const LaunchDesc &P, int64_t r
 // 16 k .. 16 k + 15, lane l taking row 16 k + l/4, value columns
 // 32 w + 8 (l%4) .. +7 (LDS: slice + 1 KiB k + 16 l).
 // sm_lds is the LDS byte address of the workgroup's Smem.
+template <int K0 = 0, int K1 = 2>
 __device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const LaunchDesc &P, int64_t row, int lc, int H,
                                       int h, int w, const Lane &L) {
     const uint16_t *vg = static_cast<const uint16_t *>(P.v);
     const uint64_t base = uniform64(reinterpret_cast<uint64_t>(vg + (row * H + h) * DV + 32 * w));
     const uint32_t lim = (uint32_t)(lc - 1) * (uint32_t)(H * DV * 2) + L.vldc;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = K0; k < K1; ++k)
         dma16(base, min(L.vld[k], lim), sm_lds + OFF_VR + (uint32_t)(((vb * NW + w) * C * 32 + 16 * k * 32) * 2));
 }
 
@@ -464,10 +471,11 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
     for (int i = 0; i < 2; ++i) {
         const int t = 16 * i + (tid >> 4);
         const bool live = t < lc;
-        convert_row<true>(sm, kbuf + L.cvt[i], pf.k[i], live, nullptr);
+        const uint32_t raw = OFF_KQR + (uint32_t)(t * DK * 2 + 16 * L.n16);
+        convert_row<true>(sm, kbuf + L.cvt[i], lds_ld<uint4>(sm, raw), live, nullptr);
         if (WANT_Q) {
             float kqv = 1.f;
-            convert_row<NORM_Q>(sm, qbuf + L.cvt[i], pf.q[i], live, &kqv);
+            convert_row<NORM_Q>(sm, qbuf + L.cvt[i], lds_ld<uint4>(sm, raw + C * DK * 2), live, &kqv);
             if (!NORM_Q && L.n16 == 0) sm.kq[pb][t] = kqv;
         }
     }
@@ -574,7 +582,7 @@ __device__ __forceinline__ floatx4 key_side_a10t(const Smem &sm, int pb, const L
 // the fp16 band and stored as (row s, column t).
 __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L) {
     const int lane = L.lane;
-    const float4 a = sm.tpart[pb][0][lane], bq = sm.tpart[pb][1][lane], cq = sm.tpart[pb][2][lane];
+    const float4 a = sm.tpart[0][lane], bq = sm.tpart[1][lane], cq = sm.tpart[2][lane];
     const floatx4 T00 = {a.x, a.y, a.z, a.w}, T11t = {bq.x, bq.y, bq.z, bq.w}, A10t = {cq.x, cq.y, cq.z, cq.w};
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
     const floatx4 W = mm16(h4(A10t), h4(T00), z);
@@ -600,12 +608,12 @@ __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L
         t10 *= sc;
         t11 *= sc;
     }
-    _Float16 *tt = sm.tT[pb];
+    _Float16 *tt = sm.tT;
     *reinterpret_cast<half4 *>(&tt[c * C + rb]) = h4(t00);        // t = rb + j, s = c
     *reinterpret_cast<half4 *>(&tt[c * C + 16 + rb]) = h4(t10);   // t = 16 + rb + j, s = c
 #pragma unroll
     for (int j = 0; j < 4; ++j) tt[(16 + rb + j) * C + 16 + c] = (_Float16)t11[j];  // t = 16 + c, s = 16 + rb + j
-    if (lane == 0) sm.tsc[pb] = ldexpf(1.f, -eT);
+    if (lane == 0) sm.tsc = ldexpf(1.f, -eT);
 }
 
 // ---- key side, part 3 (wave 1): P -> fp16, transposed -------------------------
@@ -660,7 +668,7 @@ __device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, const La
         r = key_side_tile(sm, pb, w >> 1, L);
         slot = w >> 1;
     }
-    sm.tpart[pb][slot][L.lane] = make_float4(r[0], r[1], r[2], r[3]);
+    sm.tpart[slot][L.lane] = make_float4(r[0], r[1], r[2], r[3]);
 }
 
 // ---- state-side operand reads ---------------------------------------------------
@@ -687,6 +695,22 @@ __device__ __forceinline__ void store_state(float *dst_head, const floatx16 (&Sa
             *reinterpret_cast<float4 *>(dst + 32 * a + 8 * q4 + 4 * hi32) =
                 make_float4(Sacc[a][4 * q4] * sc, Sacc[a][4 * q4 + 1] * sc, Sacc[a][4 * q4 + 2] * sc,
                             Sacc[a][4 * q4 + 3] * sc);
+}
+
+// Full token rows 8 w .. 8 w + 7 of a staged output tile (V buffer vbuf) to
+// obase (the chunk's first row, head h, column 0); rows at or past lc are
+// skipped.  Non-temporal: the outputs are not read again.
+__device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, char *obase, int lc, uint32_t hdv2, int w,
+                                             const Lane &L) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t tile = OFF_VR + (uint32_t)(vbuf * NW * C * 32 * 2);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const i16x4_t lo = tr4u(sm, tile + L.orr[k][0]), hi = tr4u(sm, tile + L.orr[k][1]);
+        const u32x4 row = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (size_t)(8 * w + 4 * k) * hdv2 + L.ost);
+        if (lc == C || 8 * w + 4 * k + (L.n16 & 3) < lc) __builtin_nontemporal_store(row, dst);
+    }
 }
 
 template <bool WANT_O, bool NORM_Q>
@@ -756,7 +780,7 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     // The upper-right 16x16 blocks of T^T and P^T (s >= 16, t < 16) stay zero.
     for (int idx = tid; idx < 16 * 16; idx += NT) {
         const int o = (16 + (idx >> 4)) * C + (idx & 15);
-        sm.tT[0][o] = sm.tT[1][o] = (_Float16)0.f;
+        sm.tT[o] = (_Float16)0.f;
         sm.pT[0][o] = sm.pT[1][o] = (_Float16)0.f;
     }
 
@@ -769,28 +793,35 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     int vb = 0;  // V buffer of the current chunk
     if (cur.lc > 0) {
         dma_v(sm_lds, 0, P, row0 + cur.t0, cur.lc, H, h, w, L);
-        if (nx.lc > 0) dma_v(sm_lds, 1, P, row0 + nx.t0, nx.lc, H, h, w, L);
-        load_kq<WANT_O>(pf, P, row0 + cur.t0, cur.lc, H, h, w, L);
+        load_kq<0>(pf, sm_lds, P, row0 + cur.t0, cur.lc, H, h, w, L);
+        load_kq<1, WANT_O>(pf, sm_lds, P, row0 + cur.t0, cur.lc, H, h, w, L);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the raw rows of chunk 0 have landed (each wave its own copies)
     }
     lds_barrier();
     if (cur.lc > 0) {
         key_side_convert<WANT_O, NORM_Q>(sm, 0, pf, cur.lc, tid, w, L);
-        if (nx.lc > 0) load_kq<WANT_O>(pf, P, row0 + nx.t0, nx.lc, H, h, w, L);
-        lds_barrier();
+        lds_barrier();  // the raw tiles are free again
+        if (nx.lc > 0) {
+            load_kq<0>(pf, sm_lds, P, row0 + nx.t0, nx.lc, H, h, w, L);
+            load_kq<1, WANT_O>(pf, sm_lds, P, row0 + nx.t0, nx.lc, H, h, w, L);
+        }
         key_side_tasks<WANT_O>(sm, 0, w, L);
     }
 
-    int p = 0;         // key-side buffer of the current chunk
-    bool tail2 = false;  // the last two vector-memory operations issued are output stores
+    int p = 0;  // key-side buffer of the current chunk
+    // outputs of the previous chunk, staged in V buffer vb_pend, are stored after the next barrier
+    char *obase_pend = nullptr;
+    int lc_pend = 0, vb_pend = 0;
     while (cur.lc > 0) {
         const Chunk nx2 = next_chunk(P, nx, len, ne_end);
+        // every load this wave issued has landed; the barrier then publishes the
+        // raw key/query rows and the staged outputs to all waves
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();  // key-side tasks of `cur` complete; previous state step done
-        // every load issued before this point has landed (outputs of the previous
-        // chunk, the last two operations when tail2 is set, may still be in flight)
-        if (WANT_O && tail2)
-            __builtin_amdgcn_s_waitcnt(0x0F72);
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (WANT_O && lc_pend > 0) {
+            store_o_rows(sm, vb_pend, obase_pend, lc_pend, hdv2, w, L);
+            lc_pend = 0;
+        }
         // ---- state side of `cur` ------------------------------------------------
         const int lc = cur.lc;
         const uint32_t kbuf = OFF_KH + p * KBUF;  // keys of `cur`; queries at + 2 KBUF
@@ -861,22 +892,29 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         if (w == 3) key_side_combine(sm, p, L);
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
         // operands of `cur` that are complete now are read before the tasks
-        const half8 tfr0 = tr_frag_st(sm, OFF_TT + p * (C * C * 2), 0, L);
-        const half8 tfr1 = tr_frag_st(sm, OFF_TT + p * (C * C * 2), 1, L);
+        const half8 tfr0 = tr_frag_st(sm, OFF_TT, 0, L);
+        const half8 tfr1 = tr_frag_st(sm, OFF_TT, 1, L);
         half8 pfr0, pfr1;
         if (WANT_O) {
             pfr0 = tr_frag_st(sm, OFF_PT + p * (C * C * 2), 0, L);
             pfr1 = tr_frag_st(sm, OFF_PT + p * (C * C * 2), 1, L);
         }
-        const float tsc = sm.tsc[p];
+        const float tsc = sm.tsc;
         const float gCp = sm.gC[p];
-        if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
-        // loads of `nx2` (V copies first: their count is fixed, see the wait above)
-        if (nx2.lc > 0) {
-            const int vb2 = vb == 0 ? 2 : vb - 1;  // (vb + 2) % 3
-            dma_v(sm_lds, vb2, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
-            load_kq<WANT_O>(pf, P, row0 + nx2.t0, nx2.lc, H, h, w, L);
+        // raw keys of `nx2` before the task, queries (and gates) after it; all
+        // before the output stores (see the wait above)
+        const bool has2 = nx2.lc > 0;
+        const int64_t krow2 = row0 + (has2 ? nx2.t0 : cur.t0);
+        const int klc2 = has2 ? nx2.lc : cur.lc;
+        load_kq<0>(pf, sm_lds, P, krow2, klc2, H, h, w, L);
+        // V of `nx` into the other V buffer (its staged outputs went out after the
+        // first barrier; without a next chunk, rows of `cur` are copied and ignored)
+        {
+            const bool has1 = nx.lc > 0;
+            dma_v(sm_lds, vb ^ 1, P, row0 + (has1 ? nx.t0 : cur.t0), has1 ? nx.lc : cur.lc, H, h, w, L);
         }
+        if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
+        load_kq<1, WANT_O>(pf, sm_lds, P, krow2, klc2, H, h, w, L);
 
         // U = (T diag(beta)) B~
         floatx16 U = {};
@@ -958,38 +996,16 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
                         ov[4 * q4 + jj] = zz[jj] * Z[4 * q4 + jj] + pp[jj] * PO[4 * q4 + jj];
                 }
             }
-            // o_t to token rows through the wave's V slice (B~ has consumed it),
-            // then two 16-byte stores per lane
-            const uint32_t vsl = OFF_VR + (uint32_t)((vb * NW + w) * C * 32 * 2);
+            // o_t into the chunk's output tile (the V buffer, consumed by every
+            // wave's B~); full rows go out after the next barrier
+            const uint32_t tile = OFF_VR + (uint32_t)(vb * NW * C * 32 * 2);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
-                lds_st(sm, vsl + L.ow[q4],
+                lds_st(sm, tile + L.ow[q4],
                        make_uint2(pack_bf16(ov[4 * q4], ov[4 * q4 + 1]), pack_bf16(ov[4 * q4 + 2], ov[4 * q4 + 3])));
-            uint4 orow[2];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const i16x4_t lo = tr4u(sm, vsl + L.orr[k][0]), hi = tr4u(sm, vsl + L.orr[k][1]);
-                orow[k] = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-            char *ob = reinterpret_cast<char *>(og + ((row0 + cur.t0) * H + h) * DV + 32 * w);  // wave-uniform
-            // a fresh 32-bit lane offset, so that the stores take the uniform base
-            // in SGPRs (not a 64-bit address per lane)
-            uint32_t ost = L.ost;
-            asm volatile("" : "+v"(ost));
-            if (lc == C) {
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    char *obk = ob + (size_t)(16 * k) * hdv2;
-                    *reinterpret_cast<uint4 *>(obk + ost) = orow[k];
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    char *obk = ob + (size_t)(16 * k) * hdv2;
-                    if (16 * k + L.n16 < lc) *reinterpret_cast<uint4 *>(obk + ost) = orow[k];
-                }
-            }
-            tail2 = lc == C;
+            obase_pend = reinterpret_cast<char *>(og + ((row0 + cur.t0) * H + h) * DV);  // wave-uniform
+            lc_pend = lc;
+            vb_pend = vb;
         }
         // W' = 2^{sig1} 2^{g_C - g_s} u_s (Sacc units), then Sacc <- Sacc 2^{-delta} + K^ T W'
 #pragma unroll
@@ -1018,9 +1034,13 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         cur = nx;
         nx = nx2;
         p ^= 1;
-        vb = vb == 2 ? 0 : vb + 1;
+        vb ^= 1;
     }
 
+    if (WANT_O && lc_pend > 0) {
+        lds_barrier();  // the last staged outputs are complete
+        store_o_rows(sm, vb_pend, obase_pend, lc_pend, hdv2, w, L);
+    }
     store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
