@@ -713,11 +713,12 @@ __device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, char *oba
     }
 }
 
-template <bool WANT_O, bool NORM_Q>
-__global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
+// One wave's part of a (request, head).  ROLE is the wave index: it selects
+// the wave's value rows and key-side task, and as a compile-time constant it
+// removes the per-chunk role branches.
+template <int ROLE, bool WANT_O, bool NORM_Q>
+__device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_t sm_lds)
 {
-    __shared__ Smem sm;
-    const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
 
     const int Lg = xcd_remap(blockIdx.x, gridDim.x);
     const int h = Lg % P.H;
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     const int b = P.req[r];
     const int H = P.H;
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    constexpr int w = ROLE;
     const Lane L = make_lane(tid, w, H);
     const int lane = L.lane, l32 = L.l32, hi32 = L.hi32;
     const int dv = 32 * w + l32;
@@ -1042,6 +1043,19 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
         store_o_rows(sm, vb_pend, obase_pend, lc_pend, hdv2, w, L);
     }
     store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
+}
+
+template <bool WANT_O, bool NORM_Q>
+__global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
+{
+    __shared__ Smem sm;
+    const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+        case 0: wave_main<0, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 1: wave_main<1, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 2: wave_main<2, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        default: wave_main<3, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+    }
 }
 
 }  // namespace
