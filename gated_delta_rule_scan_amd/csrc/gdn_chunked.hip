@@ -77,6 +77,7 @@ typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) void lvoid_t;
+typedef __attribute__((address_space(1))) char gchar;  // global memory (so that no flat access is emitted)
 
 constexpr int C = 32;        // tokens per chunk
 constexpr int DK = 128;
@@ -122,8 +123,10 @@ static_assert(OFF_QH == OFF_KH + 2 * KBUF, "query tiles follow the key tiles");
 // free of bank conflicts: one unit of 32 consecutive rows (16-byte reads, which
 // the LDS serves in 16-lane groups), four consecutive tokens x 64 bytes
 // (transposed 8-byte reads, served 32 lanes at a time) and 16 rows x units
-// 4g + ks, g = lane / 16 (the tile tasks).
-__device__ __forceinline__ int krow(int t) { return ((4 * (t & 3) + (t >> 2)) & 15) | (t & 16); }
+// 4g + ks, g = lane / 16 (the tile tasks).  Within each half of the tile the
+// order is a 4 x 4 transpose, so rows 4 b + j (j = 0..3) of a 4-row block sit
+// at 4 j + b % 4 (+16 for b >= 4): one lane term plus a constant per block.
+__device__ __forceinline__ int krow(int t) { return 4 * (t & 3) + ((t >> 2) & 3) + (t & 16); }
 __device__ __forceinline__ int sqd(int q) { return ((q & 1) << 1) | (q >> 1); }
 
 __device__ __forceinline__ void lds_barrier() {
@@ -279,7 +282,7 @@ struct Lane {
     uint32_t yz;        // Y/Z A fragments: row krow(l32), unit hi32 (+32 bytes per step)
     uint32_t kt[2][2];  // K^T A fragments: [k-step hf][token + 8]
     uint32_t task[2];   // tile-task fragments of rows 16 b + lane%16 (+16 bytes per k-step)
-    uint32_t cvt[2];    // conversion stores of rows 16 i + tid/16
+    uint32_t cvt;       // conversion stores of row 4 b + lane/16, block b = 0 (krow)
     uint32_t st;        // transposed reads of T^T / P^T
     uint32_t vrd;       // transposed reads of the wave's V slice
     uint32_t cwr;       // this wave's coefficient rows, lane half hi32
@@ -325,8 +328,7 @@ __device__ __forceinline__ Lane make_lane(int tid, int w, int H) {
     }
     L.task[0] = krow(n) * KROWB + 64 * g;
     L.task[1] = krow(16 + n) * KROWB + 64 * g;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) L.cvt[i] = krow(16 * i + 4 * w + g) * KROWB + 32 * (n >> 1) + 8 * (n & 1);
+    L.cvt = krow(g) * KROWB + 32 * (n >> 1) + 8 * (n & 1);
     L.st = 64 * (4 * (g >> 1) + (n >> 2)) + 2 * (16 * (g & 1) + 4 * (n & 3));
     L.vrd = 64 * (4 * (g >> 1) + (n >> 2)) + 32 * (g & 1) + 8 * (n & 3);
     L.cwr = OFF_CW + w * 4 * C * 4 + 16 * L.hi32;
@@ -374,31 +376,42 @@ struct Pref {
     uint16_t ga, gb;   // wave 1: alpha, beta of token lane%32
 };
 
+// Byte addresses of the span's first token (head h) in each packed tensor and
+// the byte strides between consecutive tokens; a chunk starting at span token
+// t0 is at base + t0 * stride.
+struct Bases {
+    uint64_t k, q, v, a, b, o;  // v: the wave's 32 value columns
+    uint32_t ts;                // H d * 2 (rows of q, k, v, o; d_k = d_v = d)
+    uint32_t tg;                // H * 2 (alpha, beta)
+};
+__device__ __forceinline__ uint64_t at_tok(uint64_t base, int t0, uint32_t stride) {
+    return base + (uint64_t)(uint32_t)t0 * stride;
+}
+
 // Keys (and queries) of a chunk into the raw tiles: wave w copies rows
 // 8 w .. 8 w + 7, 1 KiB (4 rows) per copy, lane l taking row 8 w + 4 j + l/16,
 // columns 8 (l%16) .. +7.  Rows past the chunk are clamped to its last row
 // (always in the span), so that every copy is issued; their values are ignored
-// by the consumers.  The gates (wave 1) go to registers.  row (int64) is the
-// packed row of the chunk's first token.
+// by the consumers.  The gates (wave 1) go to registers.  t0 is the chunk's
+// first span token.
 // WHICH = 0: keys; 1: queries (when COPY) and, from wave 1, the gates.
 template <int WHICH, bool COPY = true>
-__device__ __forceinline__ void load_kq(Pref &pf, uint32_t sm_lds, const LaunchDesc &P, int64_t row, int lc, int H,
-                                        int h, int w, const Lane &L) {
-    const int64_t e0 = (row * H + h) * DK;  // element offset of (row, head)
-    const uint64_t base = uniform64(reinterpret_cast<uint64_t>(static_cast<const uint16_t *>(WHICH ? P.q : P.k) + e0));
-    const uint32_t lim = (uint32_t)(lc - 1) * (uint32_t)(H * DK * 2) + L.ldc;
+__device__ __forceinline__ void load_kq(Pref &pf, uint32_t sm_lds, const Bases &G, int t0, int lc, int w,
+                                        const Lane &L) {
+    const uint64_t base = at_tok(WHICH ? G.q : G.k, t0, G.ts);
+    const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.ldc;
     if (COPY) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             dma16(base, min(L.ld[j], lim), sm_lds + OFF_KQR + (uint32_t)((WHICH * C + 8 * w + 4 * j) * DK * 2));
     }
     if (WHICH == 1 && w == 1) {
-        const int64_t g0 = row * H + h;
-        const char *ab = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.alpha) + g0);
-        const char *bb = reinterpret_cast<const char *>(static_cast<const uint16_t *>(P.beta) + g0);
-        const uint32_t off = min(L.gld, (uint32_t)((lc - 1) * H * 2));
-        pf.ga = *reinterpret_cast<const uint16_t *>(ab + off);
-        pf.gb = *reinterpret_cast<const uint16_t *>(bb + off);
+        typedef __attribute__((address_space(1))) const uint16_t gu16;
+        const gchar *ab = (const gchar *)at_tok(G.a, t0, G.tg);
+        const gchar *bb = (const gchar *)at_tok(G.b, t0, G.tg);
+        const uint32_t off = min(L.gld, (uint32_t)(lc - 1) * G.tg);
+        pf.ga = *(gu16 *)(ab + off);
+        pf.gb = *(gu16 *)(bb + off);
     }
 }
 
@@ -407,11 +420,10 @@ __device__ __forceinline__ void load_kq(Pref &pf, uint32_t sm_lds, const LaunchD
 // 32 w + 8 (l%4) .. +7 (LDS: slice + 1 KiB k + 16 l).
 // sm_lds is the LDS byte address of the workgroup's Smem.
 template <int K0 = 0, int K1 = 2>
-__device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const LaunchDesc &P, int64_t row, int lc, int H,
-                                      int h, int w, const Lane &L) {
-    const uint16_t *vg = static_cast<const uint16_t *>(P.v);
-    const uint64_t base = uniform64(reinterpret_cast<uint64_t>(vg + (row * H + h) * DV + 32 * w));
-    const uint32_t lim = (uint32_t)(lc - 1) * (uint32_t)(H * DV * 2) + L.vldc;
+__device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const Bases &G, int t0, int lc, int w,
+                                      const Lane &L) {
+    const uint64_t base = at_tok(G.v, t0, G.ts);
+    const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.vldc;
 #pragma unroll
     for (int k = K0; k < K1; ++k)
         dma16(base, min(L.vld[k], lim), sm_lds + OFF_VR + (uint32_t)(((vb * NW + w) * C * 32 + 16 * k * 32) * 2));
@@ -463,22 +475,37 @@ __device__ __forceinline__ void convert_row(Smem &sm, uint32_t dst, uint4 raw, b
     lds_st(sm, dst + 16, hi);
 }
 
-template <bool WANT_Q, bool NORM_Q>
-__device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &pf, int lc, int tid, int w,
-                                                 const Lane &L) {
+// Conversion work of a chunk in 4-row blocks: block b of the keys (and, with
+// outputs, of the queries) covers tokens 4 b .. 4 b + 3, lane l converting
+// token 4 b + l/16, columns 8 (l%16) .. +7.  Wave 3, which also finishes T in
+// this phase, and wave 1, which also forms the gate sums, take fewer blocks.
+template <bool WANT_Q>
+__device__ constexpr int cvt_owner(int gi) {  // gi: block gi/2 of keys (gi even) or queries
+    return WANT_Q ? (gi < 5 ? 0 : gi < 10 ? 2 : gi < 13 ? 1 : 3) : (gi >> 1);
+}
+
+template <bool WANT_Q, bool NORM_Q, int W>
+__device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &pf, int lc, const Lane &L) {
     const uint32_t kbuf = OFF_KH + pb * KBUF, qbuf = OFF_QH + pb * KBUF;
+    constexpr int NG = WANT_Q ? 16 : 8;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = 16 * i + (tid >> 4);
+    for (int gi = 0; gi < NG; ++gi) {
+        if (cvt_owner<WANT_Q>(gi) != W) continue;
+        const int kind = WANT_Q ? (gi & 1) : 0;
+        const int rb = WANT_Q ? (gi >> 1) : gi;
+        const int t = 4 * rb + L.g;
         const bool live = t < lc;
-        const uint32_t raw = OFF_KQR + (uint32_t)(t * DK * 2 + 16 * L.n16);
-        convert_row<true>(sm, kbuf + L.cvt[i], lds_ld<uint4>(sm, raw), live, nullptr);
-        if (WANT_Q) {
+        const uint32_t raw = OFF_KQR + (uint32_t)(kind * C * DK * 2 + rb * 4 * DK * 2) + 16 * L.lane;
+        const uint32_t dst = (kind ? qbuf : kbuf) + L.cvt + (uint32_t)(((rb & 3) + 16 * (rb >> 2)) * KROWB);
+        if (kind == 0) {
+            convert_row<true>(sm, dst, lds_ld<uint4>(sm, raw), live, nullptr);
+        } else {
             float kqv = 1.f;
-            convert_row<NORM_Q>(sm, qbuf + L.cvt[i], lds_ld<uint4>(sm, raw + C * DK * 2), live, &kqv);
+            convert_row<NORM_Q>(sm, dst, lds_ld<uint4>(sm, raw), live, &kqv);
             if (!NORM_Q && L.n16 == 0) sm.kq[pb][t] = kqv;
         }
     }
+    constexpr int w = W;
     if (w == 1) {
         const int tl = L.l32;
         const bool live = tl < lc;
@@ -601,7 +628,7 @@ __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L
         t11[j] = T11t[j] * b1v[j];
         mx = fmaxf(mx, fmaxf(fabsf(t00[j]), fmaxf(fabsf(t10[j]), fabsf(t11[j]))));
     }
-    const int eT = f16_adjust(wave_max(mx));
+    const int eT = out_of_band(mx) ? f16_adjust(wave_max(mx)) : 0;
     if (eT != 0) {
         const float sc = ldexpf(1.f, eT);
         t00 *= sc;
@@ -700,7 +727,7 @@ __device__ __forceinline__ void store_state(float *dst_head, const floatx16 (&Sa
 // Full token rows 8 w .. 8 w + 7 of a staged output tile (V buffer vbuf) to
 // obase (the chunk's first row, head h, column 0); rows at or past lc are
 // skipped.  Non-temporal: the outputs are not read again.
-__device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, char *obase, int lc, uint32_t hdv2, int w,
+__device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, gchar *obase, int lc, uint32_t hdv2, int w,
                                              const Lane &L) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const uint32_t tile = OFF_VR + (uint32_t)(vbuf * NW * C * 32 * 2);
@@ -708,7 +735,8 @@ __device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, char *oba
     for (int k = 0; k < 2; ++k) {
         const i16x4_t lo = tr4u(sm, tile + L.orr[k][0]), hi = tr4u(sm, tile + L.orr[k][1]);
         const u32x4 row = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (size_t)(8 * w + 4 * k) * hdv2 + L.ost);
+        typedef __attribute__((address_space(1))) u32x4 gu32x4;
+        gu32x4 *dst = (gu32x4 *)(obase + (size_t)(8 * w + 4 * k) * hdv2 + L.ost);
         if (lc == C || 8 * w + 4 * k + (L.n16 & 3) < lc) __builtin_nontemporal_store(row, dst);
     }
 }
@@ -730,12 +758,21 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     const Lane L = make_lane(tid, w, H);
     const int lane = L.lane, l32 = L.l32, hi32 = L.hi32;
     const int dv = 32 * w + l32;
-    uint16_t *og = static_cast<uint16_t *>(P.o);
-    const uint32_t hdv2 = (uint32_t)(H * DV * 2);
-
     const int len = P.len[r];
     const int64_t row0 = P.row0[r];
     const int ne_end = P.emit_begin[r + 1];
+    Bases G;
+    {
+        const uint64_t th = (uint64_t)(row0 * H + h);  // token-head index of the span's first token
+        G.ts = (uint32_t)(H * DK * 2);
+        G.tg = (uint32_t)(H * 2);
+        G.k = uniform64(reinterpret_cast<uint64_t>(P.k) + th * (DK * 2));
+        G.q = uniform64(reinterpret_cast<uint64_t>(P.q) + th * (DK * 2));
+        G.v = uniform64(reinterpret_cast<uint64_t>(P.v) + th * (DV * 2) + 64 * w);
+        G.o = uniform64(reinterpret_cast<uint64_t>(P.o) + th * (DV * 2));
+        G.a = uniform64(reinterpret_cast<uint64_t>(P.alpha) + th * 2);
+        G.b = uniform64(reinterpret_cast<uint64_t>(P.beta) + th * 2);
+    }
 
     // ---- state S^T = 2^{-sigma} Sacc: tile a covers d_k rows 32a..32a+31; the
     // lane holds value row dv and d_k rows 8(j/4) + 4*hi32 + j%4 of each tile.
@@ -793,25 +830,25 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     Pref pf;
     int vb = 0;  // V buffer of the current chunk
     if (cur.lc > 0) {
-        dma_v(sm_lds, 0, P, row0 + cur.t0, cur.lc, H, h, w, L);
-        load_kq<0>(pf, sm_lds, P, row0 + cur.t0, cur.lc, H, h, w, L);
-        load_kq<1, WANT_O>(pf, sm_lds, P, row0 + cur.t0, cur.lc, H, h, w, L);
+        dma_v(sm_lds, 0, G, cur.t0, cur.lc, w, L);
+        load_kq<0>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
+        load_kq<1, WANT_O>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the raw rows of chunk 0 have landed (each wave its own copies)
     }
     lds_barrier();
     if (cur.lc > 0) {
-        key_side_convert<WANT_O, NORM_Q>(sm, 0, pf, cur.lc, tid, w, L);
+        key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
         lds_barrier();  // the raw tiles are free again
         if (nx.lc > 0) {
-            load_kq<0>(pf, sm_lds, P, row0 + nx.t0, nx.lc, H, h, w, L);
-            load_kq<1, WANT_O>(pf, sm_lds, P, row0 + nx.t0, nx.lc, H, h, w, L);
+            load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
+            load_kq<1, WANT_O>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
         }
         key_side_tasks<WANT_O>(sm, 0, w, L);
     }
 
     int p = 0;  // key-side buffer of the current chunk
     // outputs of the previous chunk, staged in V buffer vb_pend, are stored after the next barrier
-    char *obase_pend = nullptr;
+    gchar *obase_pend = nullptr;
     int lc_pend = 0, vb_pend = 0;
     while (cur.lc > 0) {
         const Chunk nx2 = next_chunk(P, nx, len, ne_end);
@@ -820,7 +857,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();  // key-side tasks of `cur` complete; previous state step done
         if (WANT_O && lc_pend > 0) {
-            store_o_rows(sm, vb_pend, obase_pend, lc_pend, hdv2, w, L);
+            store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
             lc_pend = 0;
         }
         // ---- state side of `cur` ------------------------------------------------
@@ -830,7 +867,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         float *cwl = sm.cw[w][0];
 
         // key side of `nx`: conversion (independent of the state chain above)
-        if (nx.lc > 0) key_side_convert<WANT_O, NORM_Q>(sm, p ^ 1, pf, nx.lc, tid, w, L);
+        if (nx.lc > 0) key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
         // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
         // (all fragments are read first, so that the reads overlap)
         half8 kf[8], qf[8];
@@ -905,17 +942,17 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         // raw keys of `nx2` before the task, queries (and gates) after it; all
         // before the output stores (see the wait above)
         const bool has2 = nx2.lc > 0;
-        const int64_t krow2 = row0 + (has2 ? nx2.t0 : cur.t0);
+        const int kt2 = has2 ? nx2.t0 : cur.t0;
         const int klc2 = has2 ? nx2.lc : cur.lc;
-        load_kq<0>(pf, sm_lds, P, krow2, klc2, H, h, w, L);
+        load_kq<0>(pf, sm_lds, G, kt2, klc2, w, L);
         // V of `nx` into the other V buffer (its staged outputs went out after the
         // first barrier; without a next chunk, rows of `cur` are copied and ignored)
         {
             const bool has1 = nx.lc > 0;
-            dma_v(sm_lds, vb ^ 1, P, row0 + (has1 ? nx.t0 : cur.t0), has1 ? nx.lc : cur.lc, H, h, w, L);
+            dma_v(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, w, L);
         }
         if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
-        load_kq<1, WANT_O>(pf, sm_lds, P, krow2, klc2, H, h, w, L);
+        load_kq<1, WANT_O>(pf, sm_lds, G, kt2, klc2, w, L);
 
         // U = (T diag(beta)) B~
         floatx16 U = {};
@@ -1004,7 +1041,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             for (int q4 = 0; q4 < 4; ++q4)
                 lds_st(sm, tile + L.ow[q4],
                        make_uint2(pack_bf16(ov[4 * q4], ov[4 * q4 + 1]), pack_bf16(ov[4 * q4 + 2], ov[4 * q4 + 3])));
-            obase_pend = reinterpret_cast<char *>(og + ((row0 + cur.t0) * H + h) * DV);  // wave-uniform
+            obase_pend = (gchar *)at_tok(G.o, cur.t0, G.ts);  // wave-uniform
             lc_pend = lc;
             vb_pend = vb;
         }
@@ -1040,7 +1077,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
 
     if (WANT_O && lc_pend > 0) {
         lds_barrier();  // the last staged outputs are complete
-        store_o_rows(sm, vb_pend, obase_pend, lc_pend, hdv2, w, L);
+        store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
     }
     store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
 }
