@@ -558,13 +558,15 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = rb + j;
-        const bool lower = r > c, same8 = ((r ^ c) & 8) == 0;
+        const bool lower = r > c, upper = r < c, same8 = ((r ^ c) & 8) == 0;
         const float d = glv[j] - gls;
-        const float val = r == c ? 0.f : (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * G[j];
+        // computed on every lane (the diagonal is dropped by the selects), so
+        // that no branch splits the task
+        const float val = (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * G[j];
         N[j] = (lower && same8) ? val : 0.f;
-        Nt[j] = (!lower && same8) ? val : 0.f;
+        Nt[j] = (upper && same8) ? val : 0.f;
         Lw[j] = (lower && !same8) ? val : 0.f;
-        Lt[j] = (!lower && !same8) ? val : 0.f;
+        Lt[j] = (upper && !same8) ? val : 0.f;
     }
     const half4 Nh = h4(N), Nth = h4(Nt), Lh = h4(Lw), Lth = h4(Lt);
     const floatx4 N2 = mm16(Nth, Nh, z);     // N N
@@ -668,9 +670,10 @@ __device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = rb + j;
-        x00[j] = c <= r ? exp2_(gt0[j] - g0) * P00[j] : 0.f;
+        const float e00 = exp2_(gt0[j] - g0) * P00[j], e11 = exp2_(gt1[j] - g1) * P11[j];
+        x00[j] = c <= r ? e00 : 0.f;
         x10[j] = exp2_(gt1[j] - g0) * P10[j];
-        x11[j] = c <= r ? exp2_(gt1[j] - g1) * P11[j] : 0.f;
+        x11[j] = c <= r ? e11 : 0.f;
     }
     _Float16 *pt = sm.pT[pb];
     *reinterpret_cast<half4 *>(&pt[c * C + rb]) = h4(x00);
