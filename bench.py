@@ -98,6 +98,34 @@ def cpu_baseline(w, spans, budget_s: float = 15.0):
                       f"fp64 C rank-1 oracle with OpenMP; {dt:.1f} s wall"}
 
 
+def planner_bench(gdn):
+    """Host planner: wall time of the O(N M) placement and the expected
+    recomputation it reaches against the balanced placement and no checkpoint."""
+    import numpy as np
+
+    def dists(N):
+        x = np.arange(N + 1) / N
+        u = np.r_[0.0, np.full(N, 1.0 / N)]
+        bimodal = np.exp(-((x - 0.35) / 0.04) ** 2) + np.exp(-((x - 0.75) / 0.08) ** 2) + 0.02
+        bimodal[0] = 0.05
+        head = 0.9995 ** np.arange(N + 1)
+        return {"uniform": u, "bimodal": bimodal / bimodal.sum(), "geometric": head / head.sum()}
+
+    for N, M in [(8192, 8), (32768, 16), (65536, 16), (262144, 64)]:
+        for name, p in dists(N).items():
+            reps = 3
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                pos, cost = gdn.plan_checkpoints(p, M)
+            ms = (time.perf_counter() - t0) / reps * 1e3
+            bal = gdn.expected_recompute(p, gdn.balanced_checkpoints(N, M))
+            none = gdn.expected_recompute(p, [])
+            print(json.dumps({"metric": "checkpoint placement (host planner)", "distribution": name,
+                              "N": N, "M": M, "ms": round(ms, 3), "ns_per_NM": round(ms * 1e6 / (N * M), 3),
+                              "expected_recompute": {"planned": cost, "balanced": bal, "none": none},
+                              "planned_vs_balanced": cost / bal if bal > 0 else None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +140,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the replay, time a plain device copy of this many MiB "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
+    ap.add_argument("--planner", action="store_true",
+                    help="instead of the replay, time the host checkpoint-placement planner and "
+                         "print one JSON line per (distribution, N, M)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -125,6 +156,9 @@ def main():
     import workloads as W
 
     gdn.load()
+    if args.planner:
+        planner_bench(gdn)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_probe_mib:

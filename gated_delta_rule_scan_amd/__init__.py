@@ -24,6 +24,7 @@ __all__ = [
     "GDNError", "NORMALIZE_K", "NORMALIZE_Q", "KERNEL_RECURRENT", "KERNEL_CHUNKED",
     "MAX_CHECKPOINTS", "library_path", "load", "version", "kernel_for", "tail_len", "select_checkpoint",
     "tail_replay", "resume", "prefill_emit_checkpoints",
+    "expected_recompute", "balanced_checkpoints", "plan_checkpoints",
 ]
 
 NORMALIZE_K = 1
@@ -84,6 +85,13 @@ def load():
     lib.gdn_prefill_emit_checkpoints.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p,
                                                  ctypes.c_int32, vp, vp, vp, vp]
     lib.gdn_prefill_emit_checkpoints.restype = ctypes.c_int
+    f64p = ctypes.POINTER(ctypes.c_double)
+    lib.gdn_expected_recompute.argtypes = [f64p, ctypes.c_int64, i64p, ctypes.c_int32]
+    lib.gdn_expected_recompute.restype = ctypes.c_double
+    lib.gdn_balanced_checkpoints.argtypes = [ctypes.c_int64, ctypes.c_int32, i64p]
+    lib.gdn_balanced_checkpoints.restype = ctypes.c_int32
+    lib.gdn_plan_checkpoints.argtypes = [f64p, ctypes.c_int64, ctypes.c_int32, i64p, f64p]
+    lib.gdn_plan_checkpoints.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -120,6 +128,37 @@ def select_checkpoint(positions: Sequence[int], depth: int) -> int:
     """1-based index of the deepest checkpoint <= depth (0: none); -1 if invalid."""
     pos = _i64(positions)
     return int(load().gdn_select_checkpoint(_p64(pos), int(pos.size), int(depth)))
+
+
+def _f64(seq) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(seq, dtype=np.float64).reshape(-1))
+
+
+def expected_recompute(p: Sequence[float], positions: Sequence[int]) -> float:
+    """R(p, C): expected recomputed tokens for depth weights p[0..N] and the
+    checkpoint positions (host computation in the library); -1.0 if invalid."""
+    pa, pos = _f64(p), _i64(positions)
+    return float(load().gdn_expected_recompute(pa.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                               pa.size - 1, _p64(pos), int(pos.size)))
+
+
+def balanced_checkpoints(N: int, M: int) -> np.ndarray:
+    """M positions floor(i (N+1) / (M+1)): gaps that differ by at most one."""
+    out = np.zeros(max(int(M), 0), dtype=np.int64)
+    if int(load().gdn_balanced_checkpoints(int(N), int(M), _p64(out))) != 0:
+        raise GDNError(1, f"invalid balanced placement N={N} M={M}")
+    return out
+
+
+def plan_checkpoints(p: Sequence[float], M: int):
+    """Optimal M positions for depth weights p[0..N] (O(N M) dynamic programme).
+    Returns (positions int64 [M], minimal expected recomputation)."""
+    pa = _f64(p)
+    out = np.zeros(max(int(M), 0), dtype=np.int64)
+    cost = ctypes.c_double(0.0)
+    _check(load().gdn_plan_checkpoints(pa.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), pa.size - 1,
+                                       int(M), _p64(out), ctypes.byref(cost)))
+    return out, float(cost.value)
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -1,6 +1,6 @@
 """Build libgdnreplay.so in-tree with hipcc for gfx950.
 
-Every .hip file under csrc/ is compiled to an object (in parallel) and linked
+Every .hip and .cpp file under csrc/ is compiled to an object (in parallel) and linked
 into gated_delta_rule_scan_amd/libgdnreplay.so.  Packed-FP32 instruction
 selection is switched off for device code (the hardware forms of those
 instructions are not used by this library).
@@ -44,7 +44,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"

@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "../../include/gdnreplay.h"
+#include "gdn_error.h"
 #include "gdn_launch.h"
 
 #define GDN_API extern "C" __attribute__((visibility("default")))
@@ -31,14 +32,19 @@ namespace {
 
 thread_local std::string g_last_error;
 
-gdn_status fail(gdn_status st, const char *fmt, ...) {
+gdn_status vfail(gdn_status st, const char *fmt, va_list ap) {
     char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
     vsnprintf(buf, sizeof(buf), fmt, ap);
-    va_end(ap);
     g_last_error = buf;
     return st;
+}
+
+gdn_status fail(gdn_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    const gdn_status r = vfail(st, fmt, ap);
+    va_end(ap);
+    return r;
 }
 
 bool valid_width(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -227,6 +233,14 @@ int32_t select_exact(const int64_t *pos, int32_t M, int64_t depth) {
 }
 
 }  // namespace
+
+gdn_status gdn::host_fail(gdn_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    const gdn_status r = vfail(st, fmt, ap);
+    va_end(ap);
+    return r;
+}
 
 GDN_API const char *gdn_version(void) { return "libgdnreplay 0.1.0 gfx950"; }
 

@@ -174,6 +174,46 @@ gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape,
                                         float *ckpt_states, float *state_out, void *o,
                                         hipStream_t stream);
 
+/*
+ * Checkpoint placement ([SPC] §3 problem statement, §4 Theorems 1 and 2).
+ * Host only, double precision, no device work.  A depth distribution p is an
+ * array of N + 1 non-negative finite weights p[0..N] (p[0] is the weight of
+ * a miss, d = 0; p need not sum to one).  Positions are M strictly increasing
+ * integers in [1, N]; the implicit c_0 = 0 is the zero state.
+ */
+
+/*
+ * Expected recomputation R(p, C) = sum_{d=0}^{N} p[d] (d - max({0} u {c_i <= d}))
+ * ([SPC] §3, the gap form R(p, g) with c_i the partial sums of g).  Returns
+ * -1.0 if p is NULL, N < 0, M < 0, pos is NULL with M > 0, a weight is negative
+ * or not finite, or the positions are not strictly increasing in [1, N].
+ */
+double gdn_expected_recompute(const double *p, int64_t N, const int64_t *pos, int32_t M);
+
+/*
+ * Balanced placement ([SPC] §4 Theorem 1: optimal for p uniform on 1..N):
+ * pos_out[i-1] = floor(i (N + 1) / (M + 1)), i = 1..M, so the M + 1 gaps
+ * (summing to N + 1) differ by at most one.  pos_out: host [M].  Returns 0, or
+ * -1 if N < 0, M < 0, M > N or pos_out is NULL with M > 0.
+ */
+int32_t gdn_balanced_checkpoints(int64_t N, int32_t M, int64_t *pos_out);
+
+/*
+ * Optimal placement for any p ([SPC] §4 Theorem 2): M positions minimising
+ * R(p, C), by the dynamic programme over the last checkpoint with the convex
+ * hull trick, O(N M) time and 4 M (N + 2) bytes of host memory (allocated and
+ * freed inside the call).  Where several placements reach the minimum any one
+ * of them is returned.
+ *   p         host [N + 1]
+ *   pos_out   host [M] (written), strictly increasing in [1, N]
+ *   cost_out  host, nullable: receives the minimal R(p, C)
+ * Errors: GDN_ERR_INVALID_ARGUMENT for a NULL p or pos_out (M > 0), N < 1,
+ * M outside 0..N, or a negative or non-finite weight; GDN_ERR_UNSUPPORTED
+ * when N + 2 or M (N + 2) exceeds 2^28.
+ */
+gdn_status gdn_plan_checkpoints(const double *p, int64_t N, int32_t M, int64_t *pos_out,
+                                double *cost_out);
+
 #ifdef __cplusplus
 }
 #endif

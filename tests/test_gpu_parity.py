@@ -301,3 +301,44 @@ def test_emitted_states_resume_exactly(gdn):
         torch.cuda.synchronize()
         rel = (r["state"][0] - rp["ckpt"][0, 0]).norm() / rp["ckpt"][0, 0].norm()
         assert rel < 1e-5, (dpt, float(rel))
+
+
+def test_planned_checkpoints_drive_prefill_and_resume(gdn):
+    """The placement planner feeds the prefill's emission positions; resumes at
+    depths drawn from the same distribution select the oracle's checkpoint,
+    recompute exactly f_g(d) tokens and match the fp64 oracle's state at d."""
+    from oracle import planner as OP
+    N, M = 900, 6
+    x = np.arange(N + 1) / N
+    p = np.exp(-((x - 0.35) / 0.04) ** 2) + np.exp(-((x - 0.75) / 0.08) ** 2) + 0.02
+    p[0] = 0.05
+    p /= p.sum()
+    pos, cost = gdn.plan_checkpoints(p, M)
+    want, _ = OP.dp_optimum(p, M)
+    assert cost == pytest.approx(want, rel=1e-9)
+    w = W.prefill(seed=31, B=1, H=2, d=128, N=N, M=M, dtype="bf16", positions=[pos.tolist()])
+    PT.to_device(w)
+    _log(f"[planned] prefill N={N} positions={pos.tolist()}")
+    full = PT.run_library(gdn, w)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    depths = rng.choice(np.arange(N + 1), 6, p=p).tolist() + [int(pos[2]), int(pos[2]) + 1]
+    tensors = (w.q, w.k, w.v, w.alpha, w.beta)
+    total = 0
+    for dpt in depths:
+        wr = W.Workload(**{**w.__dict__, "op": "resume", "ckpt_states": full["ckpt"], "depth": [dpt]})
+        r = PT.run_library(gdn, wr)
+        torch.cuda.synchronize()
+        j = r["j"][0]
+        assert j == oracle.select_checkpoint(pos.tolist(), dpt)
+        c_j = 0 if j == 0 else int(pos[j - 1])
+        assert dpt - c_j == OP.recompute_len(pos.tolist(), dpt)
+        total += dpt - c_j
+        for h in range(w.H):
+            (q, k, v, a, bt), _ = PT.pair_inputs(w, 0, h, (1, dpt), tensors)
+            S, _, _ = oracle.scan_rank1(np.zeros((w.dv, w.dk)), q, k, v, a, bt, normalize_k=True)
+            got = PT.np64(r["state"][0, h])
+            ref = np.linalg.norm(S)
+            err = np.linalg.norm(got - S) / ref if ref > 0 else np.abs(got).max()
+            assert err < PT.TOL["bf16"], (dpt, h, err)
+    _log(f"[planned] depths={depths} recomputed={total} expected/req={cost:.1f}")

@@ -107,3 +107,133 @@ def test_lemma1_lipschitz():
         vp, _ = OP.dp_optimum(p, M)
         vq, _ = OP.dp_optimum(q, M)
         assert abs(vp - vq) <= N * tv + 1e-12
+
+
+# ---- the library's planner against the oracle --------------------------------
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_delta_rule_scan_amd as g
+    g.load()
+    return g
+
+
+def _families(rng, N):
+    yield "uniform", _uniform(N)
+    yield "random", rng.random(N + 1)
+    sparse = rng.random(N + 1) * (rng.random(N + 1) < 0.2)
+    yield "sparse", sparse
+    yield "geometric", 0.97 ** np.arange(N + 1)
+    yield "spikes", np.bincount(rng.integers(0, N + 1, 5), minlength=N + 1).astype(float)
+    yield "zero", np.zeros(N + 1)
+
+
+def test_lib_expected_recompute_matches_oracle(gdn):
+    rng = np.random.default_rng(6)
+    for _ in range(100):
+        N = int(rng.integers(0, 80))
+        M = int(rng.integers(0, N + 1))
+        p = rng.random(N + 1)
+        pos = sorted(rng.choice(np.arange(1, N + 1), M, replace=False).tolist()) if M else []
+        assert gdn.expected_recompute(p, pos) == pytest.approx(OP.expected_recompute(p, pos), rel=1e-12, abs=1e-12)
+    # invalid placements and weights are rejected
+    assert gdn.expected_recompute([0.1, 0.2, 0.3], [2, 2]) == -1.0
+    assert gdn.expected_recompute([0.1, 0.2, 0.3], [3]) == -1.0
+    assert gdn.expected_recompute([0.1, -0.2, 0.3], [1]) == -1.0
+    assert gdn.expected_recompute([0.1, float("nan"), 0.3], [1]) == -1.0
+
+
+def test_lib_balanced_is_theorem1_placement(gdn):
+    for N, M in [(1, 1), (2, 1), (10, 3), (8192, 8), (32768, 16), (65536, 16), (100, 100)]:
+        pos = gdn.balanced_checkpoints(N, M).tolist()
+        assert pos == OP.gaps_to_positions(OP.balanced_gaps(N, M))
+        g = OP.positions_to_gaps(pos, N)
+        assert sum(g) == N + 1 and min(g) >= 1 and max(g) - min(g) <= 1
+    with pytest.raises(Exception):
+        gdn.balanced_checkpoints(3, 4)
+
+
+@pytest.mark.parametrize("N", [1, 2, 7, 40, 150])
+def test_lib_plan_matches_dp_oracle(gdn, N):
+    rng = np.random.default_rng(100 + N)
+    for M in sorted({0, 1, 2, 3, 5, 8, N} & set(range(N + 1))):
+        for name, p in _families(rng, N):
+            pos, cost = gdn.plan_checkpoints(p, M)
+            want, _ = OP.dp_optimum(p, M)
+            scale = max(1.0, float(np.sum(p)) * N)
+            assert cost == pytest.approx(want, rel=1e-9, abs=1e-12 * scale), (name, N, M)
+            pos = pos.tolist()
+            assert len(pos) == M and all(1 <= x <= N for x in pos) and pos == sorted(set(pos))
+            # the returned placement reaches the minimum
+            assert OP.expected_recompute(p, pos) == pytest.approx(want, rel=1e-9, abs=1e-12 * scale)
+
+
+def test_lib_plan_is_a_brute_force_optimum(gdn):
+    rng = np.random.default_rng(7)
+    for _ in range(80):
+        N = int(rng.integers(1, 10))
+        M = int(rng.integers(0, min(N, 4) + 1))
+        p = rng.random(N + 1) * (rng.random(N + 1) < 0.6)
+        best, argmins = OP.brute_force_optimum(p, M, rel_tol=1e-9)
+        pos, cost = gdn.plan_checkpoints(p, M)
+        assert cost == pytest.approx(best, rel=1e-9, abs=1e-12)
+        assert tuple(pos.tolist()) in argmins
+
+
+def _recompute_vec(p, pos):
+    """R by the definition, vectorised over depths (test helper)."""
+    N = len(p) - 1
+    d = np.arange(N + 1)
+    c = np.r_[0, np.asarray(pos, dtype=np.int64)]
+    last = c[np.searchsorted(c, d, side="right") - 1]
+    return float(np.dot(p, d - last))
+
+
+def test_lib_plan_large_sizes(gdn):
+    """N = 65536, M = 16 (the prefill-with-emission shape): the plan's cost is
+    what its positions give, no single checkpoint moved by one position does
+    better, it beats the balanced and random placements, and for uniform p it
+    ties the balanced placement (Theorem 1)."""
+    rng = np.random.default_rng(8)
+    N, M = 65536, 16
+    x = np.arange(N + 1) / N
+    p = np.exp(-((x - 0.3) / 0.05) ** 2) + 0.5 * np.exp(-((x - 0.8) / 0.02) ** 2) + 0.05
+    p[0] = 0.1
+    p /= p.sum()
+    t0 = time.perf_counter()
+    pos, cost = gdn.plan_checkpoints(p, M)
+    dt = time.perf_counter() - t0
+    assert dt < 5.0, dt
+    pos = pos.tolist()
+    assert cost == pytest.approx(_recompute_vec(p, pos), rel=1e-9)
+    for i in range(M):
+        for step in (-1, 1):
+            q = list(pos)
+            q[i] += step
+            if (i > 0 and q[i] <= q[i - 1]) or (i + 1 < M and q[i] >= q[i + 1]) or not (1 <= q[i] <= N):
+                continue
+            assert _recompute_vec(p, q) >= cost - 1e-9 * cost
+    bal = gdn.balanced_checkpoints(N, M)
+    assert cost <= _recompute_vec(p, bal) + 1e-12
+    for _ in range(5):
+        rnd = np.sort(rng.choice(np.arange(1, N + 1), M, replace=False))
+        assert cost <= _recompute_vec(p, rnd) + 1e-12
+    pu = _uniform(N)
+    posu, costu = gdn.plan_checkpoints(pu, M)
+    assert costu == pytest.approx(_recompute_vec(pu, bal), rel=1e-9)
+    g = OP.positions_to_gaps(posu.tolist(), N)
+    assert max(g) - min(g) <= 1
+
+
+def test_lib_plan_edge_cases_and_errors(gdn):
+    p = np.r_[0.0, np.ones(10)]
+    pos, cost = gdn.plan_checkpoints(p, 0)
+    assert pos.size == 0 and cost == pytest.approx(sum(range(11)))
+    pos, cost = gdn.plan_checkpoints(p, 10)
+    assert pos.tolist() == list(range(1, 11)) and cost == 0.0
+    pos, cost = gdn.plan_checkpoints(np.zeros(11), 3)
+    assert cost == 0.0 and pos.tolist() == sorted(set(pos.tolist()))
+    for bad_p, M in [([1.0], 0), (p, 11), (p, -1), (np.r_[p[:-1], -1.0], 2), (np.r_[p[:-1], np.inf], 2)]:
+        with pytest.raises(gdn.GDNError) as e:
+            gdn.plan_checkpoints(bad_p, M)
+        assert e.value.status == 1
