@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "GDNError", "NORMALIZE_K", "NORMALIZE_Q", "KERNEL_RECURRENT", "KERNEL_CHUNKED",
     "MAX_CHECKPOINTS", "library_path", "load", "version", "kernel_for", "tail_len", "select_checkpoint",
-    "tail_replay", "resume", "prefill_emit_checkpoints",
+    "tail_replay", "tail_replay_with_h2d", "resume", "prefill_emit_checkpoints",
     "expected_recompute", "balanced_checkpoints", "plan_checkpoints",
 ]
 
@@ -79,6 +79,10 @@ def load():
     lib.gdn_tail_replay.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p, ctypes.c_int64,
                                     ctypes.c_int64, vp, vp, i64p, vp]
     lib.gdn_tail_replay.restype = ctypes.c_int
+    lib.gdn_tail_replay_with_h2d.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p, ctypes.c_int64,
+                                             ctypes.c_int64, vp, vp, i64p, vp, vp, ctypes.c_size_t,
+                                             vp, vp, vp]
+    lib.gdn_tail_replay_with_h2d.restype = ctypes.c_int
     lib.gdn_resume.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p, ctypes.c_int32, vp,
                                i64p, vp, vp, i32p, vp]
     lib.gdn_resume.restype = ctypes.c_int
@@ -240,6 +244,37 @@ def tail_replay(q, k, v, alpha, beta, tok_offset, m, r_num, r_den, *, first_pos=
                                   _ptr(v), _ptr(alpha), _ptr(beta), _p64(off), _p64(fp), _p64(mm),
                                   int(r_num), int(r_den), _ptr(state_out), _ptr(o), _p64(kout),
                                   _stream(k.device)))
+    return state_out, o, [int(x) for x in kout]
+
+
+def tail_replay_with_h2d(q, k, v, alpha, beta, tok_offset, m, r_num, r_den, kv_src, kv_dst,
+                         copy_stream, copy_done, *, first_pos=None, flags=NORMALIZE_K,
+                         state_out=None, o=None, want_o=True):
+    """tail_replay on the current stream, overlapped with a host-to-device copy of
+    kv_src (pinned CPU tensor) into kv_dst (device tensor of the same byte size)
+    on copy_stream; the current stream waits for the copy (copy_done, a
+    torch.cuda.Event) before any later work.  Returns what tail_replay returns."""
+    if want_o and o is None:
+        o = torch.empty_like(v)
+    rows, H, dk, dv, dt = _check_tensors(q if o is not None else None, k, v, alpha, beta, o)
+    nbytes = kv_src.numel() * kv_src.element_size()
+    if kv_src.is_cuda or not kv_dst.is_cuda or not kv_src.is_contiguous() or not kv_dst.is_contiguous():
+        raise ValueError("kv_src must be a contiguous host tensor and kv_dst a contiguous device tensor")
+    if kv_dst.numel() * kv_dst.element_size() != nbytes:
+        raise ValueError("kv_src and kv_dst differ in byte size")
+    if not copy_done.cuda_event:
+        copy_done.record(copy_stream)  # torch creates the event on its first record
+    mm = _i64(m)
+    B = int(mm.size)
+    off, fp = _rows_meta(tok_offset, first_pos, rows, B)
+    state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
+    kout = np.zeros(B, np.int64)
+    sh = _shape(B, H, dk, dv, dt, flags)
+    _check(load().gdn_tail_replay_with_h2d(
+        ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _p64(off), _p64(fp), _p64(mm), int(r_num), int(r_den), _ptr(state_out), _ptr(o), _p64(kout),
+        ctypes.c_void_p(kv_dst.data_ptr()), ctypes.c_void_p(kv_src.data_ptr()), nbytes,
+        _stream(k.device), ctypes.c_void_p(copy_stream.cuda_stream), ctypes.c_void_p(copy_done.cuda_event)))
     return state_out, o, [int(x) for x in kout]
 
 

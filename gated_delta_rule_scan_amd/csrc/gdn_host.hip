@@ -262,13 +262,12 @@ GDN_API int32_t gdn_select_checkpoint(const int64_t *pos, int32_t M, int64_t dep
     return select_exact(pos, M, depth);
 }
 
-GDN_API gdn_status gdn_tail_replay(const gdn_shape *shape, const void *q, const void *k,
-                                   const void *v, const void *alpha, const void *beta,
-                                   const int64_t *h_tok_offset, const int64_t *h_first_pos,
-                                   const int64_t *h_m, int64_t r_num, int64_t r_den,
-                                   float *state_out, void *o, int64_t *h_k_out,
-                                   hipStream_t stream) {
-    g_last_error.clear();
+namespace {
+
+// Validation and span logic of a tail replay; fills work and ks (B entries).
+gdn_status prepare_tail(const gdn_shape *shape, const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                        const int64_t *h_m, int64_t r_num, int64_t r_den, std::vector<Work> &work,
+                        std::vector<int64_t> &ks) {
     gdn_status st = check_shape(shape);
     if (st != GDN_OK) return st;
     if (shape->B == 0) return GDN_OK;
@@ -277,8 +276,8 @@ GDN_API gdn_status gdn_tail_replay(const gdn_shape *shape, const void *q, const 
     if (r_num < 0 || r_den <= 0)
         return fail(GDN_ERR_INVALID_ARGUMENT, "replay ratio %lld/%lld invalid", (long long)r_num,
                     (long long)r_den);
-    std::vector<Work> work(shape->B);
-    std::vector<int64_t> ks(shape->B);
+    work.assign(shape->B, Work{});
+    ks.assign(shape->B, 0);
     for (int32_t b = 0; b < shape->B; ++b) {
         if (h_m[b] < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "h_m[%d] < 0", b);
         const int64_t kb = tail_len_exact(h_m[b], r_num, r_den);
@@ -290,10 +289,59 @@ GDN_API gdn_status gdn_tail_replay(const gdn_shape *shape, const void *q, const 
         if ((st = span_to_rows(b, h_tok_offset, h_first_pos, h_m[b] - kb + 1, kb, &w.row0)) != GDN_OK)
             return st;
     }
+    return GDN_OK;
+}
+
+}  // namespace
+
+GDN_API gdn_status gdn_tail_replay(const gdn_shape *shape, const void *q, const void *k,
+                                   const void *v, const void *alpha, const void *beta,
+                                   const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                                   const int64_t *h_m, int64_t r_num, int64_t r_den,
+                                   float *state_out, void *o, int64_t *h_k_out,
+                                   hipStream_t stream) {
+    g_last_error.clear();
+    std::vector<Work> work;
+    std::vector<int64_t> ks;
+    gdn_status st = prepare_tail(shape, h_tok_offset, h_first_pos, h_m, r_num, r_den, work, ks);
+    if (st != GDN_OK || shape->B == 0) return st;
     st = run(shape, q, k, v, alpha, beta, o, state_out, nullptr, nullptr, 0, work, stream);
     if (st == GDN_OK && h_k_out)
         for (int32_t b = 0; b < shape->B; ++b) h_k_out[b] = ks[b];
     return st;
+}
+
+GDN_API gdn_status gdn_tail_replay_with_h2d(const gdn_shape *shape, const void *q, const void *k,
+                                            const void *v, const void *alpha, const void *beta,
+                                            const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                                            const int64_t *h_m, int64_t r_num, int64_t r_den,
+                                            float *state_out, void *o, int64_t *h_k_out,
+                                            void *kv_dst, const void *kv_src, size_t kv_bytes,
+                                            hipStream_t stream, hipStream_t copy_stream,
+                                            hipEvent_t copy_done) {
+    g_last_error.clear();
+    std::vector<Work> work;
+    std::vector<int64_t> ks;
+    gdn_status st = prepare_tail(shape, h_tok_offset, h_first_pos, h_m, r_num, r_den, work, ks);
+    if (st != GDN_OK) return st;
+    if (kv_bytes > 0 && (!kv_dst || !kv_src))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "kv_dst or kv_src is NULL with kv_bytes = %zu", kv_bytes);
+    if (!copy_done) return fail(GDN_ERR_INVALID_ARGUMENT, "copy_done is NULL");
+    // the transfer goes first, so that the copy engine starts while the replay is queued
+    hipError_t e = hipSuccess;
+    if (kv_bytes > 0) e = hipMemcpyAsync(kv_dst, kv_src, kv_bytes, hipMemcpyHostToDevice, copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(copy_done, copy_stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "transfer: %s", hipGetErrorString(e));
+    if (shape->B > 0) {
+        st = run(shape, q, k, v, alpha, beta, o, state_out, nullptr, nullptr, 0, work, stream);
+        if (st != GDN_OK) return st;
+    }
+    // work queued on `stream` after this call sees both the replayed states and the transfer
+    e = hipStreamWaitEvent(stream, copy_done, 0);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "join: %s", hipGetErrorString(e));
+    if (h_k_out)
+        for (int32_t b = 0; b < shape->B; ++b) h_k_out[b] = ks[b];
+    return GDN_OK;
 }
 
 GDN_API gdn_status gdn_resume(const gdn_shape *shape, const void *q, const void *k,

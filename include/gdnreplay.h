@@ -134,6 +134,34 @@ gdn_status gdn_tail_replay(const gdn_shape *shape,
                            hipStream_t stream);
 
 /*
+ * Tail replay overlapped with the host-to-device transfer of the attention
+ * layers' KV cache ([TR] §2.5, "transfer and replay overlap": the replay needs
+ * only the tail inputs, so the KV copy and the replay run on separate streams
+ * and join before the new suffix is processed).  In this order it queues
+ *   1. hipMemcpyAsync(kv_dst, kv_src, kv_bytes, host to device) on copy_stream
+ *      (skipped when kv_bytes = 0), then hipEventRecord(copy_done, copy_stream);
+ *   2. the replay of gdn_tail_replay (same arguments, same results) on stream;
+ *   3. hipStreamWaitEvent(stream, copy_done): later work on `stream` sees both.
+ * kv_src should be pinned host memory (hipHostMalloc) for the copy to run
+ * asynchronously; kv_dst is device memory of kv_bytes; copy_done is an event
+ * created by the caller (the library creates and keeps none).  The streams
+ * should be distinct for the two to overlap.  Errors: those of gdn_tail_replay
+ * (nothing queued), GDN_ERR_INVALID_ARGUMENT for a NULL copy_done or a NULL
+ * kv_dst / kv_src with kv_bytes > 0 (nothing queued), GDN_ERR_HIP when a
+ * runtime call fails (earlier steps may have been queued).
+ */
+typedef struct ihipEvent_t *hipEvent_t;
+gdn_status gdn_tail_replay_with_h2d(const gdn_shape *shape,
+                                    const void *q, const void *k, const void *v,
+                                    const void *alpha, const void *beta,
+                                    const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                                    const int64_t *h_m, int64_t r_num, int64_t r_den,
+                                    float *state_out, void *o, int64_t *h_k_out,
+                                    void *kv_dst, const void *kv_src, size_t kv_bytes,
+                                    hipStream_t stream, hipStream_t copy_stream,
+                                    hipEvent_t copy_done);
+
+/*
  * Resume from a sparse checkpoint ([SPC] §3): for each request b,
  * j_b = gdn_select_checkpoint(h_ckpt_pos + b*M, M, h_depth[b]); the scan
  * starts from ckpt_states[b][j_b - 1] (or from zero when j_b = 0) and

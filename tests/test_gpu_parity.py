@@ -342,3 +342,68 @@ def test_planned_checkpoints_drive_prefill_and_resume(gdn):
             err = np.linalg.norm(got - S) / ref if ref > 0 else np.abs(got).max()
             assert err < PT.TOL["bf16"], (dpt, h, err)
     _log(f"[planned] depths={depths} recomputed={total} expected/req={cost:.1f}")
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+def test_tail_replay_with_h2d_matches_plain(gdn, kernel):
+    """The overlapped entry point ([TR] §2.5) gives the plain replay's results
+    bit for bit, and the transfer lands intact before later work on the stream."""
+    w = W.tail(seed=41, B=3, H=4, d=128, m=2000, m_list=[2000, 777, 1500])
+    PT.to_device(w)
+    flags = w.flags | KERNELS[kernel]
+    S0, O0, k0 = gdn.tail_replay(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m, w.r_num, w.r_den,
+                                 first_pos=w.first_pos, flags=flags)
+    n = 3 << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8).pin_memory()
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    S1, O1, k1 = gdn.tail_replay_with_h2d(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m, w.r_num,
+                                          w.r_den, src, dst, cs, ev, first_pos=w.first_pos, flags=flags)
+    chk = dst.sum(dtype=torch.int64)  # queued on the current stream, after the join
+    torch.cuda.synchronize()
+    assert k1 == k0
+    assert torch.equal(S1, S0) and torch.equal(O1, O0)
+    assert int(chk) == int(src.sum(dtype=torch.int64)) and torch.equal(dst.cpu(), src)
+
+
+def test_tail_replay_with_h2d_overlaps(gdn):
+    """[TR] §2.5 latency model: with the KV transfer on its own stream the two
+    take about max(T_KV, T_replay), less than the serial sum."""
+    w = W.config(3, device="cuda")
+    st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
+    o = torch.empty_like(w.v)
+    n = 32 << 20
+    src = torch.empty(n, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    cur = torch.cuda.current_stream()
+
+    def replay():
+        gdn.tail_replay(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m, w.r_num, w.r_den,
+                        first_pos=w.first_pos, flags=w.flags, state_out=st, o=o)
+
+    def timed(fn, reps=7):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            fn()
+            b.record(cur)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    for _ in range(20):
+        replay()
+    t_rep = timed(replay)
+    t_kv = timed(lambda: dst.copy_(src, non_blocking=True))
+    t_ser = timed(lambda: (dst.copy_(src, non_blocking=True), replay()))
+    t_ov = timed(lambda: gdn.tail_replay_with_h2d(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m,
+                                                  w.r_num, w.r_den, src, dst, cs, ev, first_pos=w.first_pos,
+                                                  flags=w.flags, state_out=st, o=o))
+    _log(f"[overlap] T_replay={t_rep:.3f} T_KV={t_kv:.3f} serial={t_ser:.3f} overlapped={t_ov:.3f} ms")
+    assert t_ov < t_ser
+    assert t_ov <= 1.15 * max(t_kv, t_rep) + 0.05
