@@ -407,3 +407,43 @@ def test_tail_replay_with_h2d_overlaps(gdn):
     _log(f"[overlap] T_replay={t_rep:.3f} T_KV={t_kv:.3f} serial={t_ser:.3f} overlapped={t_ov:.3f} ms")
     assert t_ov < t_ser
     assert t_ov <= 1.15 * max(t_kv, t_rep) + 0.05
+
+
+@pytest.mark.parametrize("alpha_rng", [(0.98, 0.99), (0.95, 1.0)])
+def test_tail_replay_error_against_full_run(gdn, alpha_rng):
+    """Diagnostic of [TR] §2.3: the zero-start tail replay misses exactly
+    E_m = (T_m ... T_{a+1}) S_a, a = m - k.  On the GPU, ||S_m - S^_m||_F (full
+    prefill vs tail replay) matches the fp64 oracle's value, and with unit keys,
+    beta in [0, 2] and alpha <= rho it obeys ||E_m||_F <= rho^k ||S_a||_F."""
+    m, B, H = 4096, 2, 4
+    k = oracle.tail_length(m, 5, 100)
+    a = m - k
+    w = W.prefill(seed=43, B=B, H=H, d=128, N=m, M=1, dtype="bf16", alpha_rng=alpha_rng,
+                  beta_hi=2.0, positions=[[a]] * B)
+    PT.to_device(w)
+    full = PT.run_library(gdn, w)  # S_a (emitted) and S_m (final)
+    S_hat, _, ks = gdn.tail_replay(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, [m] * B, 5, 100,
+                                   first_pos=w.first_pos, flags=w.flags, want_o=False)
+    torch.cuda.synchronize()
+    assert ks == [k] * B
+    S_m, S_a = full["state"].double(), full["ckpt"][:, 0].double()
+    E = S_m - S_hat.double()
+    for b in range(B):
+        rho = float(w.alpha[w.tok_offset[b] + a:w.tok_offset[b] + m].float().max())
+        for h in range(H):
+            e_gpu = float(E[b, h].norm())
+            (q, kk, v, al, bt), _ = PT.pair_inputs(w, b, h, (1, m))
+            S_full, _, st = oracle.scan_rank1(np.zeros((128, 128)), q, kk, v, al, bt, normalize_k=True,
+                                              emit_after=[a])
+            S_tail, _, _ = oracle.scan_rank1(np.zeros((128, 128)), q[a:], kk[a:], v[a:], al[a:], bt[a:],
+                                             normalize_k=True)
+            e_ref = float(np.linalg.norm(S_full - S_tail))
+            sm = float(np.linalg.norm(S_full))
+            # each GPU state is within 3e-3 of the oracle's (relative), so is their difference
+            assert abs(e_gpu - e_ref) <= 2 * PT.TOL["bf16"] * sm, (b, h, e_gpu, e_ref)
+            bound = rho ** k * float(np.linalg.norm(st[a]))
+            assert e_ref <= bound * (1 + 1e-9) + 1e-12, (b, h, e_ref, bound)
+            assert e_gpu <= bound + 2 * PT.TOL["bf16"] * sm
+            if b == 0 and h == 0:
+                _log(f"[tail vs full] alpha~U{alpha_rng}: ||E||/||S_m|| gpu={e_gpu / sm:.3e} "
+                     f"oracle={e_ref / sm:.3e} bound={bound / sm:.3e} (k={k}, rho={rho:.4f})")
