@@ -24,6 +24,7 @@ __all__ = [
     "GDNError", "NORMALIZE_K", "NORMALIZE_Q", "KERNEL_RECURRENT", "KERNEL_CHUNKED",
     "MAX_CHECKPOINTS", "library_path", "load", "version", "kernel_for", "tail_len", "select_checkpoint",
     "tail_replay", "tail_replay_with_h2d", "resume", "prefill_emit_checkpoints",
+    "prefill_split_workspace_bytes", "prefill_emit_checkpoints_split",
     "expected_recompute", "balanced_checkpoints", "plan_checkpoints",
 ]
 
@@ -89,6 +90,11 @@ def load():
     lib.gdn_prefill_emit_checkpoints.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p,
                                                  ctypes.c_int32, vp, vp, vp, vp]
     lib.gdn_prefill_emit_checkpoints.restype = ctypes.c_int
+    lib.gdn_prefill_split_workspace_bytes.argtypes = [shp]
+    lib.gdn_prefill_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_prefill_emit_checkpoints_split.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p,
+                                                       ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gdn_prefill_emit_checkpoints_split.restype = ctypes.c_int
     f64p = ctypes.POINTER(ctypes.c_double)
     lib.gdn_expected_recompute.argtypes = [f64p, ctypes.c_int64, i64p, ctypes.c_int32]
     lib.gdn_expected_recompute.restype = ctypes.c_double
@@ -329,4 +335,41 @@ def prefill_emit_checkpoints(q, k, v, alpha, beta, tok_offset, ckpt_pos, *, flag
         ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
         _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o), _stream(k.device)))
+    return ckpt_states, state_out, o
+
+
+def prefill_split_workspace_bytes(B: int, H: int, dk: int, dv: int, dtype: torch.dtype = torch.bfloat16) -> int:
+    """Device bytes the split prefill needs as workspace."""
+    sh = _shape(B, H, dk, dv, _DTYPES[dtype], 0)
+    return int(load().gdn_prefill_split_workspace_bytes(ctypes.byref(sh)))
+
+
+def prefill_emit_checkpoints_split(q, k, v, alpha, beta, tok_offset, ckpt_pos, *, flags=NORMALIZE_K,
+                                   ckpt_states=None, state_out=None, o=None, want_o=True, workspace=None):
+    """prefill_emit_checkpoints with each long span cut into three segments
+    (see the C header); workspace: a device uint8 tensor of at least
+    prefill_split_workspace_bytes(...) bytes (allocated here when None).
+
+    Returns (ckpt_states [B,M,H,d_v,d_k], state_out [B,H,d_v,d_k], o or None)."""
+    if want_o and o is None:
+        o = torch.empty_like(v)
+    rows, H, dk, dv, dt = _check_tensors(q if o is not None else None, k, v, alpha, beta, o)
+    off = _i64(tok_offset)
+    B = int(off.size) - 1
+    off, _ = _rows_meta(off, None, rows, B)
+    pos = np.ascontiguousarray(np.asarray(ckpt_pos, dtype=np.int64).reshape(B, -1))
+    M = int(pos.shape[1])
+    ckpt_states = _state(ckpt_states, (B, M, H, dv, dk), k.device, "ckpt_states")
+    state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
+    sh = _shape(B, H, dk, dv, dt, flags)
+    need = int(load().gdn_prefill_split_workspace_bytes(ctypes.byref(sh)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check(load().gdn_prefill_emit_checkpoints_split(
+        ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
+        _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(k.device)))
     return ckpt_states, state_out, o

@@ -88,6 +88,7 @@ constexpr int NVB = 2;       // V staging buffers (copies run one chunk ahead)
 constexpr int KS = DK + 8;   // key/query tile row stride (halves)
 constexpr int KROWB = 2 * KS;
 constexpr int KBUF = C * KROWB;  // bytes of one key/query tile
+constexpr float kSigMax = 96.f;  // largest state exponent sigma kept between chunks (S = 2^-sigma Sacc)
 
 struct Smem {
     alignas(16) _Float16 kh[2][C * KS];  // unit keys, fp16 (layout: krow and the column order below)
@@ -203,7 +204,9 @@ __device__ __forceinline__ int f16_adjust(float mx) {
     if (!(mx > 0.f) || (mx >= 0x1p-6f && mx < 0x1p14f)) return 0;
     int E;
     frexpf(mx, &E);
-    return 8 - E;
+    // at most 2^120 up (values near the float32 denormal range are
+    // negligible next to the state they update), so 2^e stays finite
+    return min(8 - E, 120);
 }
 
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_to_f32(b); }
@@ -764,6 +767,9 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     const int len = P.len[r];
     const int64_t row0 = P.row0[r];
     const int ne_end = P.emit_begin[r + 1];
+    const int wf = P.wflags[r];
+    const bool zero_v = (wf & kWorkZeroV) != 0;        // v = 0: no V copies, V tiles zero
+    const bool out = WANT_O && !(wf & kWorkNoOut);      // outputs staged and stored
     Bases G;
     {
         const uint64_t th = (uint64_t)(row0 * H + h);  // token-head index of the span's first token
@@ -780,7 +786,14 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     // ---- state S^T = 2^{-sigma} Sacc: tile a covers d_k rows 32a..32a+31; the
     // lane holds value row dv and d_k rows 8(j/4) + 4*hi32 + j%4 of each tile.
     floatx16 Sacc[4];
-    if (P.init_off[r] >= 0) {
+    if (wf & kWorkIdentity) {
+        // lane holds d_k rows 32 a + 8 (j/4) + 4 hi32 + j%4 of value row dv
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                Sacc[a][j] = (32 * a + 8 * (j >> 2) + 4 * hi32 + (j & 3)) == dv ? 1.f : 0.f;
+    } else if (P.init_off[r] >= 0) {
         const float *src = P.init_base + P.init_off[r] + (int64_t)h * DV * DK + (int64_t)dv * DK;
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -818,6 +831,16 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         }
     }
 
+    if (zero_v) {
+        // both V buffers of this wave's columns stay zero (no copies, no output staging)
+        typedef uint32_t u32x4z __attribute__((ext_vector_type(4)));
+        const u32x4z zz = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int vbz = 0; vbz < NVB; ++vbz)
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+                lds_st(sm, OFF_VR + (uint32_t)(((vbz * NW + w) * C * 32) * 2) + 1024 * part + 16 * lane, zz);
+    }
     // The upper-right 16x16 blocks of T^T and P^T (s >= 16, t < 16) stay zero.
     for (int idx = tid; idx < 16 * 16; idx += NT) {
         const int o = (16 + (idx >> 4)) * C + (idx & 15);
@@ -833,7 +856,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     Pref pf;
     int vb = 0;  // V buffer of the current chunk
     if (cur.lc > 0) {
-        dma_v(sm_lds, 0, G, cur.t0, cur.lc, w, L);
+        if (!zero_v) dma_v(sm_lds, 0, G, cur.t0, cur.lc, w, L);
         load_kq<0>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
         load_kq<1, WANT_O>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the raw rows of chunk 0 have landed (each wave its own copies)
@@ -950,7 +973,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         load_kq<0>(pf, sm_lds, G, kt2, klc2, w, L);
         // V of `nx` into the other V buffer (its staged outputs went out after the
         // first barrier; without a next chunk, rows of `cur` are copied and ignored)
-        {
+        if (!zero_v) {
             const bool has1 = nx.lc > 0;
             dma_v(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, w, L);
         }
@@ -972,16 +995,23 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         for (int j = 0; j < 16; ++j) um = fmaxf(um, fabsf(U[j]));
         int eU = 0;
         if (out_of_band(um)) eU = f16_adjust(wave_max(um));
-        const float us = tsc * ldexpf(1.f, -eB);  // u = us * U
+        int ets;
+        frexpf(tsc, &ets);
+        const float lus = (float)(ets - 1 - eB);  // u = us U with us = tsc 2^-eB = 2^lus
 
         // scale of the new state: decay folded into sigma; rescale Sacc only
-        // when the bound on max |Sacc| would leave [1, 2^14].  The bound is kept
-        // per value column (lanes l and l ^ 32 hold the column's tokens):
-        // |K^T W'| <= 32 max|W'| and max|W'| <= max|U| us 2^sig1.
+        // when the bound on max |Sacc| would leave [1, 2^14], or when the state
+        // exponent would exceed kSigMax (a decaying state with nothing written,
+        // e.g. v = 0 or tiny gates; without the cap 2^sigma would overflow).
+        // The bound is kept per value column (lanes l and l ^ 32 hold the
+        // column's tokens): |K^T W'| <= 32 max|W'|, max|W'| <= max|U| us 2^sig1,
+        // evaluated in log2 so that no intermediate power of two overflows.
         float sig1 = sigma - gCp;
-        const float incl = 32.f * fmaxf(um, partner32(um, lane)) * us * exp2_(sig1);
-        const float mbn = mb + incl;
-        float delta = 0.f;
+        const float umx = fmaxf(um, partner32(um, lane));
+        const float linc = 5.f + log2_(umx) + lus + sig1;  // log2 of the bound (-inf when U = 0)
+        const float dmin = fmaxf(sig1 - kSigMax, 0.f);     // forced shift
+        const float mbn = mb * exp2_(-dmin) + exp2_(fminf(linc - dmin, 127.f));
+        float delta = dmin;
         if (__builtin_amdgcn_ballot_w64(mbn > 0x1p14f) != 0 ||
             (__builtin_amdgcn_ballot_w64(mbn >= 1.f) == 0 && __builtin_amdgcn_ballot_w64(mbn > 0.f) != 0)) {
             float mx = 0.f;
@@ -989,20 +1019,23 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(Sacc[a][j]));
-            const float tot = wave_max(mx) + wave_max(incl);
-            int E;
-            frexpf(tot, &E);
-            delta = (float)(E - 4);
-            mb = tot * exp2_(-delta);
+            // log2(max|Sacc| + max incl) at exponent sig1, then the shift that
+            // brings it to [8, 16), but never below the forced one
+            const float lm = log2_(wave_max(mx)), li = wave_max(linc);
+            const float hi = fmaxf(lm, li), lo = fminf(lm, li);
+            const float ltot = lo > -INFINITY ? hi + log2_(1.f + exp2_(lo - hi)) : hi;  // -inf: all zero
+            delta = fmaxf(floorf(ltot) - 3.f, sig1 - kSigMax);
+            mb = exp2_(ltot - delta);
         } else {
             mb = mbn;
         }
         sig1 -= delta;
-        const float dsc = exp2_(-delta);
+        const float dsc = exp2_(fminf(-delta, 126.f));  // Sacc is zero whenever -delta would be larger
         const bool scaled = tsc != 1.f || eB != 0 || eU != 0 || delta != 0.f;
         if (scaled && lane < 32) {
-            cwl[2 * C + lane] = sm.ws[p][lane] * exp2_(sig1) * us;  // W' = cw2 U
-            if (WANT_O) cwl[3 * C + lane] = (NORM_Q ? 1.f : sm.kq[p][lane]) * us * ldexpf(1.f, -eU);  // o (intra) = cw3 (P U')
+            // W' = cw2 U, cw2 = 2^{g_C - g_t} 2^sig1 us as one power of two
+            cwl[2 * C + lane] = exp2_(fminf(sm.gC[p] - sm.gl[p][lane] + sig1 + lus, 126.f));
+            if (WANT_O) cwl[3 * C + lane] = (NORM_Q ? 1.f : sm.kq[p][lane]) * exp2_(lus - (float)eU);  // o (intra) = cw3 (P U')
         }
 
         if (WANT_O) {
@@ -1039,14 +1072,16 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             }
             // o_t into the chunk's output tile (the V buffer, consumed by every
             // wave's B~); full rows go out after the next barrier
-            const uint32_t tile = OFF_VR + (uint32_t)(vb * NW * C * 32 * 2);
+            if (out) {
+                const uint32_t tile = OFF_VR + (uint32_t)(vb * NW * C * 32 * 2);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                lds_st(sm, tile + L.ow[q4],
-                       make_uint2(pack_bf16(ov[4 * q4], ov[4 * q4 + 1]), pack_bf16(ov[4 * q4 + 2], ov[4 * q4 + 3])));
-            obase_pend = (gchar *)at_tok(G.o, cur.t0, G.ts);  // wave-uniform
-            lc_pend = lc;
-            vb_pend = vb;
+                for (int q4 = 0; q4 < 4; ++q4)
+                    lds_st(sm, tile + L.ow[q4], make_uint2(pack_bf16(ov[4 * q4], ov[4 * q4 + 1]),
+                                                           pack_bf16(ov[4 * q4 + 2], ov[4 * q4 + 3])));
+                obase_pend = (gchar *)at_tok(G.o, cur.t0, G.ts);  // wave-uniform
+                lc_pend = lc;
+                vb_pend = vb;
+            }
         }
         // W' = 2^{sig1} 2^{g_C - g_s} u_s (Sacc units), then Sacc <- Sacc 2^{-delta} + K^ T W'
 #pragma unroll
@@ -1082,7 +1117,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         lds_barrier();  // the last staged outputs are complete
         store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
     }
-    store_state(P.state_out + ((int64_t)b * H + h) * DV * DK, Sacc, sigma, w, l32, hi32);
+    if (P.state_dst[r]) store_state(P.state_dst[r] + (int64_t)h * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
 template <bool WANT_O, bool NORM_Q>

@@ -52,14 +52,17 @@ bool valid_width(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; 
 constexpr uint32_t kKnownFlags =
     GDN_NORMALIZE_K | GDN_NORMALIZE_Q | GDN_KERNEL_RECURRENT | GDN_KERNEL_CHUNKED;
 
-// One request's work: scan `len` tokens starting at packed row `row0`, from
-// the state at `init_off` (-1: zero), emitting at span-relative counts.
+// One work item: scan `len` tokens of request b starting at packed row `row0`,
+// from the state at `init_off` (-1: zero), emitting at span-relative counts,
+// final state to dst ([H][d_v][d_k], NULL: not stored); wflags: gdn::kWork*.
 struct Work {
     int32_t b;
     int64_t row0;
     int64_t len;
     int64_t init_off;
     std::vector<std::pair<int32_t, int32_t>> emits;  // (count after, slot)
+    float *dst = nullptr;
+    int32_t wflags = 0;
 };
 
 gdn_status check_shape(const gdn_shape *s) {
@@ -149,14 +152,21 @@ int32_t kernel_choice(const gdn_shape *s) {
     return (has_chunked && !(s->flags & GDN_KERNEL_RECURRENT)) ? 1 : 0;
 }
 
+// Final states of request b go to state_out + b H d_v d_k.
+gdn_status set_state_out(std::vector<Work> &work, float *state_out, const gdn_shape *s) {
+    if (!state_out && !work.empty()) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is NULL");
+    const int64_t slot = (int64_t)s->H * s->dv * s->dk;
+    for (Work &w : work) w.dst = state_out + (int64_t)w.b * slot;
+    return GDN_OK;
+}
+
 // Validate pointers, pick the kernel and queue the launches.
 gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
-               const void *alpha, const void *beta, void *o, float *state_out,
+               const void *alpha, const void *beta, void *o,
                const float *init_base, float *emit_base, int32_t M,
                const std::vector<Work> &work, hipStream_t stream) {
     bool any_tokens = false;
     for (const Work &w : work) any_tokens |= w.len > 0;
-    if (!state_out && !work.empty()) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is NULL");
     if (any_tokens) {
         if (!k || !v || !alpha || !beta)
             return fail(GDN_ERR_INVALID_ARGUMENT, "k, v, alpha and beta must be non-NULL");
@@ -179,7 +189,6 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
     d.alpha = alpha;
     d.beta = beta;
     d.o = o;
-    d.state_out = state_out;
     d.init_base = init_base;
     d.emit_base = emit_base;
     d.H = s->H;
@@ -197,6 +206,8 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
             d.init_off[nreq] = w.init_off;
             d.len[nreq] = (int32_t)w.len;
             d.req[nreq] = w.b;
+            d.state_dst[nreq] = w.dst;
+            d.wflags[nreq] = w.wflags;
             for (const auto &e : w.emits) {
                 d.emit_after[nemit] = e.first;
                 d.emit_slot[nemit] = e.second;
@@ -305,7 +316,8 @@ GDN_API gdn_status gdn_tail_replay(const gdn_shape *shape, const void *q, const 
     std::vector<int64_t> ks;
     gdn_status st = prepare_tail(shape, h_tok_offset, h_first_pos, h_m, r_num, r_den, work, ks);
     if (st != GDN_OK || shape->B == 0) return st;
-    st = run(shape, q, k, v, alpha, beta, o, state_out, nullptr, nullptr, 0, work, stream);
+    if ((st = set_state_out(work, state_out, shape)) != GDN_OK) return st;
+    st = run(shape, q, k, v, alpha, beta, o, nullptr, nullptr, 0, work, stream);
     if (st == GDN_OK && h_k_out)
         for (int32_t b = 0; b < shape->B; ++b) h_k_out[b] = ks[b];
     return st;
@@ -324,6 +336,7 @@ GDN_API gdn_status gdn_tail_replay_with_h2d(const gdn_shape *shape, const void *
     std::vector<int64_t> ks;
     gdn_status st = prepare_tail(shape, h_tok_offset, h_first_pos, h_m, r_num, r_den, work, ks);
     if (st != GDN_OK) return st;
+    if ((st = set_state_out(work, state_out, shape)) != GDN_OK) return st;
     if (kv_bytes > 0 && (!kv_dst || !kv_src))
         return fail(GDN_ERR_INVALID_ARGUMENT, "kv_dst or kv_src is NULL with kv_bytes = %zu", kv_bytes);
     if (!copy_done) return fail(GDN_ERR_INVALID_ARGUMENT, "copy_done is NULL");
@@ -333,7 +346,7 @@ GDN_API gdn_status gdn_tail_replay_with_h2d(const gdn_shape *shape, const void *
     if (e == hipSuccess) e = hipEventRecord(copy_done, copy_stream);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "transfer: %s", hipGetErrorString(e));
     if (shape->B > 0) {
-        st = run(shape, q, k, v, alpha, beta, o, state_out, nullptr, nullptr, 0, work, stream);
+        st = run(shape, q, k, v, alpha, beta, o, nullptr, nullptr, 0, work, stream);
         if (st != GDN_OK) return st;
     }
     // work queued on `stream` after this call sees both the replayed states and the transfer
@@ -391,21 +404,19 @@ GDN_API gdn_status gdn_resume(const gdn_shape *shape, const void *q, const void 
             }
         }
     }
-    st = run(shape, q, k, v, alpha, beta, o, state_out, ckpt_states, nullptr, M, work, stream);
+    if ((st = set_state_out(work, state_out, shape)) != GDN_OK) return st;
+    st = run(shape, q, k, v, alpha, beta, o, ckpt_states, nullptr, M, work, stream);
     if (st == GDN_OK && h_j_out)
         for (int32_t b = 0; b < shape->B; ++b) h_j_out[b] = js[b];
     return st;
 }
 
-GDN_API gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape, const void *q,
-                                                const void *k, const void *v,
-                                                const void *alpha, const void *beta,
-                                                const int64_t *h_tok_offset,
-                                                const int64_t *h_first_pos,
-                                                const int64_t *h_ckpt_pos, int32_t M,
-                                                float *ckpt_states, float *state_out, void *o,
-                                                hipStream_t stream) {
-    g_last_error.clear();
+namespace {
+
+// Validation and span logic of a prefill: one work per request over 1..N_b.
+gdn_status prepare_prefill(const gdn_shape *shape, const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                           const int64_t *h_ckpt_pos, int32_t M, float *ckpt_states, float *state_out,
+                           std::vector<Work> &work) {
     gdn_status st = check_shape(shape);
     if (st != GDN_OK) return st;
     if (shape->B == 0) return GDN_OK;
@@ -417,7 +428,7 @@ GDN_API gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape, const vo
     if (M > 0 && ranges_overlap(state_out, (size_t)shape->B * slot * sizeof(float), ckpt_states,
                                 (size_t)shape->B * M * slot * sizeof(float)))
         return fail(GDN_ERR_INVALID_ARGUMENT, "state_out overlaps ckpt_states");
-    std::vector<Work> work(shape->B);
+    work.assign(shape->B, Work{});
     for (int32_t b = 0; b < shape->B; ++b) {
         if (h_first_pos && h_first_pos[b] != 1)
             return fail(GDN_ERR_INVALID_ARGUMENT, "prefill needs the whole prefix: h_first_pos[%d] = %lld",
@@ -436,5 +447,115 @@ GDN_API gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape, const vo
             w.emits.emplace_back((int32_t)c, i);
         }
     }
-    return run(shape, q, k, v, alpha, beta, o, state_out, nullptr, ckpt_states, M, work, stream);
+    return GDN_OK;
+}
+
+// Spans shorter than this run in one pass in the split prefill.
+constexpr int64_t kSplitMinTokens = 768;
+
+}  // namespace
+
+GDN_API gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape, const void *q,
+                                                const void *k, const void *v,
+                                                const void *alpha, const void *beta,
+                                                const int64_t *h_tok_offset,
+                                                const int64_t *h_first_pos,
+                                                const int64_t *h_ckpt_pos, int32_t M,
+                                                float *ckpt_states, float *state_out, void *o,
+                                                hipStream_t stream) {
+    g_last_error.clear();
+    std::vector<Work> work;
+    gdn_status st = prepare_prefill(shape, h_tok_offset, h_first_pos, h_ckpt_pos, M, ckpt_states, state_out, work);
+    if (st != GDN_OK || shape->B == 0) return st;
+    if ((st = set_state_out(work, state_out, shape)) != GDN_OK) return st;
+    return run(shape, q, k, v, alpha, beta, o, nullptr, ckpt_states, M, work, stream);
+}
+
+GDN_API size_t gdn_prefill_split_workspace_bytes(const gdn_shape *shape) {
+    if (!shape || shape->B < 0 || shape->H < 1 || shape->dk < 1 || shape->dv < 1) return 0;
+    return (size_t)4 * shape->B * shape->H * shape->dv * shape->dk * sizeof(float);
+}
+
+GDN_API gdn_status gdn_prefill_emit_checkpoints_split(const gdn_shape *shape, const void *q,
+                                                      const void *k, const void *v,
+                                                      const void *alpha, const void *beta,
+                                                      const int64_t *h_tok_offset,
+                                                      const int64_t *h_first_pos,
+                                                      const int64_t *h_ckpt_pos, int32_t M,
+                                                      float *ckpt_states, float *state_out, void *o,
+                                                      void *workspace, size_t workspace_bytes,
+                                                      hipStream_t stream) {
+    g_last_error.clear();
+    std::vector<Work> whole;
+    gdn_status st = prepare_prefill(shape, h_tok_offset, h_first_pos, h_ckpt_pos, M, ckpt_states, state_out, whole);
+    if (st != GDN_OK || shape->B == 0) return st;
+    if (shape->dk != shape->dv)
+        return fail(GDN_ERR_UNSUPPORTED, "the split prefill needs d_k = d_v (got %d, %d)", shape->dk, shape->dv);
+    const size_t need = gdn_prefill_split_workspace_bytes(shape);
+    if (!workspace || workspace_bytes < need)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    const int64_t slot = (int64_t)shape->H * shape->dv * shape->dk;
+    if (ranges_overlap(workspace, need, state_out, (size_t)shape->B * slot * sizeof(float)) ||
+        (M > 0 && ranges_overlap(workspace, need, ckpt_states, (size_t)shape->B * M * slot * sizeof(float))))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "workspace overlaps state_out or ckpt_states");
+    // workspace [4][B][H][d][d]: end of segment 0, zero-start replay and transition
+    // product of segment 1, start of segment 2
+    float *ws = static_cast<float *>(workspace);
+    const int64_t kind = (int64_t)shape->B * slot;
+    auto ws_off = [&](int which, int32_t b) { return (int64_t)which * kind + (int64_t)b * slot; };
+
+    std::vector<Work> first, second;  // launches before and after the combine
+    bool any_split = false;
+    for (Work &w : whole) {
+        const int32_t b = w.b;
+        const int64_t n = w.len;
+        float *out_b = state_out + (int64_t)b * slot;
+        const int64_t s1 = (n / 3) & ~(int64_t)31, s2 = (2 * n / 3) & ~(int64_t)31;
+        if (n < kSplitMinTokens || s1 <= 0 || s2 <= s1 || s2 >= n) {
+            w.dst = out_b;  // short span: one pass
+            first.push_back(std::move(w));
+            continue;
+        }
+        any_split = true;
+        auto segment = [&](int64_t a0, int64_t len) {
+            Work x;
+            x.b = b;
+            x.row0 = w.row0 + a0;
+            x.len = len;
+            x.init_off = -1;
+            for (const auto &e : w.emits)
+                if (e.first > a0 && e.first <= a0 + len) x.emits.emplace_back((int32_t)(e.first - a0), e.second);
+            return x;
+        };
+        Work seg0 = segment(0, s1);
+        seg0.dst = ws + ws_off(0, b);
+        Work hat1 = segment(s1, s2 - s1);
+        hat1.emits.clear();
+        hat1.wflags = gdn::kWorkNoOut;
+        hat1.dst = ws + ws_off(1, b);
+        Work prod1 = hat1;
+        prod1.wflags = gdn::kWorkNoOut | gdn::kWorkZeroV | gdn::kWorkIdentity;
+        prod1.dst = ws + ws_off(2, b);
+        Work seg1 = segment(s1, s2 - s1);
+        seg1.init_off = ws_off(0, b);
+        seg1.dst = nullptr;
+        Work seg2 = segment(s2, n - s2);
+        seg2.init_off = ws_off(3, b);
+        seg2.dst = out_b;
+        first.push_back(std::move(seg0));
+        first.push_back(std::move(hat1));
+        first.push_back(std::move(prod1));
+        second.push_back(std::move(seg1));
+        second.push_back(std::move(seg2));
+    }
+    if ((st = run(shape, q, k, v, alpha, beta, o, nullptr, ckpt_states, M, first, stream)) != GDN_OK) return st;
+    if (!any_split) return GDN_OK;
+    // start of segment 2 = (end of segment 0) P_1 + S^_1, for every request (the
+    // slots of unsplit requests are not read afterwards)
+    const hipError_t e = gdn::launch_affine_combine(ws + ws_off(0, 0), ws + ws_off(2, 0), ws + ws_off(1, 0),
+                                                    ws + ws_off(3, 0), (int64_t)shape->B * shape->H, shape->dk,
+                                                    stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+    return run(shape, q, k, v, alpha, beta, o, ws, ckpt_states, M, second, stream);
 }

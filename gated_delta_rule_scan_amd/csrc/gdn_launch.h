@@ -24,7 +24,6 @@ struct LaunchDesc {
     const void *alpha;
     const void *beta;
     void *o;                 // nullable
-    float *state_out;        // [B][H][dv][dk]
     const float *init_base;  // start states (resume); offsets below
     float *emit_base;        // emission store [B][M][H][dv][dk] (prefill)
     int32_t H;
@@ -34,7 +33,9 @@ struct LaunchDesc {
     int64_t row0[kMaxReqPerLaunch];      // packed row of the first span token
     int64_t init_off[kMaxReqPerLaunch];  // element offset of (b, slot, head 0) in init_base, -1 = zero
     int32_t len[kMaxReqPerLaunch];       // span length in tokens
-    int32_t req[kMaxReqPerLaunch];       // request index b
+    int32_t req[kMaxReqPerLaunch];       // request index b (emission store)
+    float *state_dst[kMaxReqPerLaunch];  // final state [H][dv][dk] of the work, NULL: not stored
+    int32_t wflags[kMaxReqPerLaunch];    // kWork* bits
     int32_t emit_begin[kMaxReqPerLaunch + 1];
     int32_t emit_after[kMaxEmitPerLaunch];  // span-relative token count, 1..len
     int32_t emit_slot[kMaxEmitPerLaunch];   // slot i in 0..M-1
@@ -46,6 +47,14 @@ static_assert(sizeof(LaunchDesc) <= 3584, "descriptor must fit the kernel argume
 constexpr int kNormK = 1;
 constexpr int kNormQ = 2;
 
+// Per-work flags (LaunchDesc::wflags).  The sequence-split prefill runs, for a
+// middle segment of a span, the zero-start scan (kWorkNoOut) and the product
+// of its transitions, which is the same scan with v = 0 started from the
+// identity (kWorkZeroV | kWorkNoOut | kWorkIdentity; d_k = d_v).
+constexpr int kWorkNoOut = 1;     // no outputs o (nor their stores)
+constexpr int kWorkZeroV = 2;     // v taken as zero (v is not read); implies kWorkNoOut
+constexpr int kWorkIdentity = 4;  // start state I (init_off is ignored)
+
 enum class Elem : int { F32 = 0, BF16 = 1 };
 
 // Per-token float32 kernel (any supported d_k, d_v; float32 or bf16 storage).
@@ -55,6 +64,11 @@ hipError_t launch_recurrent(const LaunchDesc &d, int dk, int dv, Elem e, hipStre
 // element type has no chunked variant.
 hipError_t launch_chunked(const LaunchDesc &d, int dk, int dv, Elem e, hipStream_t s);
 bool chunked_supported(int dk, int dv, Elem e);
+
+// out = a p + c per pair (a, c, out: [d][d] with d_v = d_k = d; p: [d][d]),
+// float32, npairs consecutive pairs; d in {16, 32, 64, 128}.
+hipError_t launch_affine_combine(const float *a, const float *p, const float *c, float *out, int64_t npairs, int d,
+                                 hipStream_t s);
 
 // Map a hardware workgroup index to a logical one so that consecutive logical
 // workgroups land on the same XCD.  Workgroups are handed to the 8 XCDs

@@ -47,14 +47,22 @@ void recurrent_kernel(const LaunchDesc P)
     const int lrow = tid / kLanesPerRow;  // local value row
     const int sub = tid % kLanesPerRow;
     const int grow = blk * DVB + lrow;    // global value row
-    const bool want_o = P.o != nullptr;
+    const int wf = P.wflags[r];
+    const bool want_o = P.o != nullptr && !(wf & kWorkNoOut);
+    const bool zero_v = (wf & kWorkZeroV) != 0;
     const int H = P.H;
 
     // Lane `sub` owns key columns (g*4 + sub)*4 .. +3 for g in [0, E4): four
     // neighbouring lanes read 64 contiguous bytes per step (no bank conflicts).
     float4 S[E4];
-    const int64_t state_row = ((int64_t)b * H + h) * DV * DK + (int64_t)grow * DK;
-    if (P.init_off[r] >= 0) {
+    if (wf & kWorkIdentity) {
+#pragma unroll
+        for (int g = 0; g < E4; ++g) {
+            const int c0 = (g * kLanesPerRow + sub) * 4;
+            S[g] = make_float4(c0 == grow ? 1.f : 0.f, c0 + 1 == grow ? 1.f : 0.f, c0 + 2 == grow ? 1.f : 0.f,
+                               c0 + 3 == grow ? 1.f : 0.f);
+        }
+    } else if (P.init_off[r] >= 0) {
         const float *src = P.init_base + P.init_off[r] + (int64_t)h * DV * DK + (int64_t)grow * DK;
 #pragma unroll
         for (int g = 0; g < E4; ++g)
@@ -86,7 +94,7 @@ void recurrent_kernel(const LaunchDesc P)
         }
         for (int idx = tid; idx < nt * DVB; idx += NT) {
             const int t = idx / DVB, c = idx % DVB;
-            sv[t][c] = to_f32(vg[((row0 + t0 + t) * H + h) * DV + blk * DVB + c]);
+            sv[t][c] = zero_v ? 0.f : to_f32(vg[((row0 + t0 + t) * H + h) * DV + blk * DVB + c]);
         }
         if (tid < nt) {
             const int64_t ab = (row0 + t0 + tid) * H + h;
@@ -156,10 +164,12 @@ void recurrent_kernel(const LaunchDesc P)
         }
     }
 
-    float *dst = P.state_out + state_row;
+    if (P.state_dst[r]) {
+        float *dst = P.state_dst[r] + (int64_t)h * DV * DK + (int64_t)grow * DK;
 #pragma unroll
-    for (int g = 0; g < E4; ++g)
-        *reinterpret_cast<float4 *>(dst + (g * kLanesPerRow + sub) * 4) = S[g];
+        for (int g = 0; g < E4; ++g)
+            *reinterpret_cast<float4 *>(dst + (g * kLanesPerRow + sub) * 4) = S[g];
+    }
 }
 
 template <int DK, int DV, typename T>

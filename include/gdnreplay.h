@@ -203,6 +203,44 @@ gdn_status gdn_prefill_emit_checkpoints(const gdn_shape *shape,
                                         hipStream_t stream);
 
 /*
+ * Workspace bytes of gdn_prefill_emit_checkpoints_split for this shape:
+ * 4 B H d_v d_k float32 values (0 for an invalid shape).  Host only.
+ */
+size_t gdn_prefill_split_workspace_bytes(const gdn_shape *shape);
+
+/*
+ * The same prefill with emission as gdn_prefill_emit_checkpoints (same
+ * arguments and results, up to rounding), for batches with few (request,
+ * head) pairs: each span of at least 768 tokens is cut into three segments
+ * (boundaries floor(N/3) and floor(2N/3), rounded down to a multiple of 32)
+ * so that three times as many workgroups share the GPU.  It uses the exact
+ * split of [TR] §2.3: the state after a segment is S_start P + S^, with P the
+ * product of the segment's transitions and S^ its zero-start replay.
+ *   1. segment 0 runs from zero with its outputs and emissions, while the
+ *      zero-start replay S^_1 and the product P_1 of segment 1 are formed (P_1
+ *      is the scan of segment 1 with v = 0 started from the identity);
+ *   2. S_start(2) = S_end(0) P_1 + S^_1 (float32);
+ *   3. segments 1 and 2 run from their start states with their outputs and
+ *      emissions.
+ * Shorter spans run in one pass in step 1.  Needs d_k = d_v.
+ *   workspace  device, >= gdn_prefill_split_workspace_bytes(shape) bytes,
+ *              owned by the caller, overwritten; must not overlap state_out
+ *              or ckpt_states.
+ * Errors: those of gdn_prefill_emit_checkpoints; GDN_ERR_UNSUPPORTED for
+ * d_k != d_v; GDN_ERR_INVALID_ARGUMENT for a NULL, small or overlapping
+ * workspace.  Nothing is queued when an error is returned before step 1.
+ */
+gdn_status gdn_prefill_emit_checkpoints_split(const gdn_shape *shape,
+                                              const void *q, const void *k, const void *v,
+                                              const void *alpha, const void *beta,
+                                              const int64_t *h_tok_offset,
+                                              const int64_t *h_first_pos,
+                                              const int64_t *h_ckpt_pos, int32_t M,
+                                              float *ckpt_states, float *state_out, void *o,
+                                              void *workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
+
+/*
  * Checkpoint placement ([SPC] §3 problem statement, §4 Theorems 1 and 2).
  * Host only, double precision, no device work.  A depth distribution p is an
  * array of N + 1 non-negative finite weights p[0..N] (p[0] is the weight of

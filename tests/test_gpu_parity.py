@@ -447,3 +447,121 @@ def test_tail_replay_error_against_full_run(gdn, alpha_rng):
             if b == 0 and h == 0:
                 _log(f"[tail vs full] alpha~U{alpha_rng}: ||E||/||S_m|| gpu={e_gpu / sm:.3e} "
                      f"oracle={e_ref / sm:.3e} bound={bound / sm:.3e} (k={k}, rho={rho:.4f})")
+
+
+# --- sequence-split prefill ----------------------------------------------------
+
+def _split_check(gdn, w, label, pairs=None):
+    PT.to_device(w)
+    _log(f"[{label}] split prefill {w.name} dtype={w.dtype} d={w.dk}")
+    C, S, O = gdn.prefill_emit_checkpoints_split(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.ckpt_pos,
+                                                 flags=w.flags)
+    C0, S0, O0 = gdn.prefill_emit_checkpoints(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.ckpt_pos,
+                                              flags=w.flags)
+    torch.cuda.synchronize()
+    pairs = _all_pairs(w) if pairs is None else pairs
+    ref = PT.oracle_pairs(w, pairs, emit=PT.emit_for(w))
+    worst = PT.compare(w, ref, S, O, C, label=label)
+    _log(f"[{label}] worst rel err {worst}; split vs one pass: state "
+         f"{float((S - S0).norm() / S0.norm()):.2e}, o {float((O.float() - O0.float()).norm() / O0.float().norm()):.2e}")
+    return S, O, C
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 32)])
+def test_split_prefill_parity(gdn, dtype, d):
+    """Three segments per span ([TR] §2.3 exact split): states, outputs and
+    emissions match the oracle's one-pass prefill, with checkpoints on both
+    segment boundaries, at the span end and inside every segment; a short span
+    in the same batch runs in one pass."""
+    lengths = [3000, 1000, 500]
+    pos = []
+    for n in lengths:
+        s1, s2 = (n // 3) & ~31, (2 * n // 3) & ~31
+        pos.append(sorted({5, s1 - 1, s1, s1 + 1, (s1 + s2) // 2, s2, s2 + 1, n}))
+    M = 8
+    assert all(len(p) == M for p in pos)
+    w = W.prefill(seed=51 + d, B=3, H=4, d=d, N=max(lengths), M=M, dtype=dtype, lengths=lengths, positions=pos)
+    _split_check(gdn, w, f"split-{dtype}-{d}")
+
+
+def test_split_prefill_full_size(gdn):
+    """The prefill workload (4 x 32 pairs, N = 65536, 16 emissions) through the
+    split path, on sampled pairs, and its time next to the one-pass prefill."""
+    w = W.config(5, device="cuda")
+    _split_check(gdn, w, "config5-split", pairs=_sample_pairs(w, 4, 5))
+    ws = torch.empty(gdn.prefill_split_workspace_bytes(w.B, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+    st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
+    ck = torch.empty(w.B, len(w.ckpt_pos[0]), w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
+    o = torch.empty_like(w.v)
+
+    def one():
+        gdn.prefill_emit_checkpoints(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.ckpt_pos, flags=w.flags,
+                                     ckpt_states=ck, state_out=st, o=o)
+
+    def split():
+        gdn.prefill_emit_checkpoints_split(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.ckpt_pos,
+                                           flags=w.flags, ckpt_states=ck, state_out=st, o=o, workspace=ws)
+
+    def t(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 3
+
+    t1, t3 = t(one), t(split)
+    _log(f"[config5-split] one pass {t1:.3f} ms, three segments {t3:.3f} ms")
+
+
+# --- extreme gates and zero values -----------------------------------------------
+
+def _with_inputs(w, alpha=None, v_zero=False):
+    if alpha is not None:
+        g = torch.Generator().manual_seed(7)
+        lo, hi = alpha
+        a = lo + (hi - lo) * torch.rand(w.alpha.shape, generator=g, dtype=torch.float64)
+        w.alpha = a.to(w.alpha.dtype)
+    if v_zero:
+        w.v = torch.zeros_like(w.v)
+    return w
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+@pytest.mark.parametrize("alpha", [(1e-4, 0.05), (0.2, 0.6)])
+def test_strong_decay_gates(gdn, kernel, alpha):
+    """Gates far below one (a chunk's decay 2^-300 and more): the old state is
+    forgotten within a few tokens and every result still matches the oracle."""
+    for op in ("tail", "resume", "prefill"):
+        w = _with_inputs(_small(op, "bf16", 128, 128, seed=61), alpha=alpha)
+        _check_workload(gdn, w, kernel, label=f"decay-{op}-{alpha[0]}")
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+def test_zero_values_decaying_state(gdn, kernel):
+    """v = 0 from a stored state: nothing is written and the state only decays.
+    Over 2^-78 it keeps its relative accuracy (oracle parity); over 2^-700,
+    far below float32, it ends as (finite) zeros instead of overflowing."""
+    w = W.resume(seed=67, B=2, H=4, d=128, N=900, M=2, dtype="bf16", alpha_rng=(0.93, 0.95),
+                 depths=[900, 880])
+    w.ckpt_pos = [[10, 20], [10, 20]]
+    w = _with_inputs(w, v_zero=True)
+    _check_workload(gdn, w, kernel, label="zero-v")
+    w = W.resume(seed=68, B=2, H=4, d=128, N=900, M=2, dtype="bf16", alpha_rng=(0.5, 0.6),
+                 depths=[900, 880])
+    w.ckpt_pos = [[10, 20], [10, 20]]
+    w = _with_inputs(w, v_zero=True)
+    PT.to_device(w)
+    res = PT.run_library(gdn, w, flags_extra=KERNELS[kernel])
+    torch.cuda.synchronize()
+    S = res["state"]
+    assert torch.isfinite(S).all() and float(S.abs().max()) < 1e-30
+    for b, (p0, n) in enumerate(PT.spans_of(w)):  # outputs exist on the span rows only
+        r0 = w.tok_offset[b] + (p0 - w.first_pos[b])
+        Ob = res["o"][r0:r0 + n].float()
+        assert torch.isfinite(Ob).all()
+        # the last 200 outputs follow at least 600 decays by <= 0.6 (< 2^-400)
+        assert float(Ob[-200:].abs().max()) < 1e-30

@@ -133,3 +133,25 @@ def test_prefill_errors(gdn):
     assert call([5], first=[2]) == 1           # prefill needs position 1
     assert call([5], states=0) == 1            # emission store missing
     assert call([5], out=FAKE) == 1            # state_out overlaps the store
+
+
+def test_split_prefill_workspace_checks(gdn):
+    lib = gdn.load()
+    sh = gdn._Shape(B=1, H=2, dk=128, dv=128, dtype=1, flags=1)
+    need = lib.gdn_prefill_split_workspace_bytes(ctypes.byref(sh))
+    assert need == 4 * 1 * 2 * 128 * 128 * 4
+    off = (ctypes.c_int64 * 2)(0, 1000)
+    pos = (ctypes.c_int64 * 1)(500)
+
+    def call(ws, nbytes, shape=sh, state=FAKE):
+        return lib.gdn_prefill_emit_checkpoints_split(
+            ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, FAKE, off, None, pos, 1, 0x200000000,
+            state, FAKE, ws, nbytes, None)
+
+    assert call(None, need) == 1
+    assert call(0x900000000, need - 1) == 1
+    # the workspace may not overlap the final states
+    assert call(0x900000000, need, state=0x900000000 + 4096) == 1
+    assert b"overlaps" in lib.gdn_last_error()
+    sh2 = gdn._Shape(B=1, H=2, dk=128, dv=64, dtype=1, flags=0)
+    assert call(0x900000000, 10 ** 9, shape=sh2) == 2
