@@ -51,10 +51,12 @@
 // float32.
 //
 // Work split: one workgroup of 4 waves per (request, head), two workgroups per
-// CU (LDS ~75 KB each).  V rows of a chunk are copied into LDS with
-// global_load_lds_dwordx4 two chunks ahead, each wave copying its own value
-// columns; key/query rows are prefetched into registers one chunk ahead;
-// outputs of a chunk are stored during the next one.
+// CU (LDS 80 KB each).  Inputs go from HBM straight into LDS with
+// global_load_lds_dwordx4: raw bf16 key and query rows two chunks ahead of
+// the state chain (converted to the fp16 tiles one chunk ahead), V rows one
+// chunk ahead; wave 3 issues the key and V copies of the whole workgroup.
+// Outputs of a chunk are staged in LDS and stored as whole rows during the
+// next one.
 //
 // Per chunk n, two barriers: after the first, the state chain of n up to B~
 // (which needs no T), the conversion of n + 1 and the last step of T for n;
@@ -430,6 +432,29 @@ __device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const Bases &G, i
 #pragma unroll
     for (int k = K0; k < K1; ++k)
         dma16(base, min(L.vld[k], lim), sm_lds + OFF_VR + (uint32_t)(((vb * NW + w) * C * 32 + 16 * k * 32) * 2));
+}
+
+// Wave 3 copies the key rows and the V columns of all four waves (the other
+// waves carry the longer tile tasks in the same phase).
+__device__ __forceinline__ void load_k_all(uint32_t sm_lds, const Bases &G, int t0, int lc, const Lane &L) {
+    const uint64_t base = at_tok(G.k, t0, G.ts);
+    const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.ldc;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            dma16(base, min(L.ld[j] - (uint32_t)(8 * (3 - w2)) * G.ts, lim),
+                  sm_lds + OFF_KQR + (uint32_t)((8 * w2 + 4 * j) * DK * 2));
+}
+__device__ __forceinline__ void dma_v_all(uint32_t sm_lds, int vb, const Bases &G, int t0, int lc, const Lane &L) {
+    const uint64_t base3 = at_tok(G.v, t0, G.ts);  // G.v holds wave 3's columns
+    const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.vldc;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            dma16(base3 - (uint64_t)(64 * (3 - w2)), min(L.vld[k], lim),
+                  sm_lds + OFF_VR + (uint32_t)(((vb * NW + w2) * C * 32 + 16 * k * 32) * 2));
 }
 
 // ---- key side, part 1 (all waves): fp16 unit keys / queries and gate sums -----
@@ -970,12 +995,12 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         const bool has2 = nx2.lc > 0;
         const int kt2 = has2 ? nx2.t0 : cur.t0;
         const int klc2 = has2 ? nx2.lc : cur.lc;
-        load_kq<0>(pf, sm_lds, G, kt2, klc2, w, L);
+        if (w == 3) load_k_all(sm_lds, G, kt2, klc2, L);
         // V of `nx` into the other V buffer (its staged outputs went out after the
         // first barrier; without a next chunk, rows of `cur` are copied and ignored)
-        if (!zero_v) {
+        if (!zero_v && w == 3) {
             const bool has1 = nx.lc > 0;
-            dma_v(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, w, L);
+            dma_v_all(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L);
         }
         if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
         load_kq<1, WANT_O>(pf, sm_lds, G, kt2, klc2, w, L);
