@@ -176,6 +176,43 @@ def overlap_bench(torch, gdn, w, dev):
         del src, dst
 
 
+def prefill_bench(torch, gdn, w, dev, args):
+    """Prefill with emission, one pass against the sequence-split path: HIP-event
+    time per call (after warm-up), tokens/s and the fraction of the HBM peak."""
+    M = len(w.ckpt_pos[0])
+    st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    ck = torch.empty(w.B, M, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    o = torch.empty_like(w.v)
+    ws = torch.empty(gdn.prefill_split_workspace_bytes(w.B, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    tokens = sum(w.n_tokens)
+    nbytes = algorithmic_bytes(tokens * w.H, w.B * w.H, w.dk, w.dv, 2) + w.B * M * w.H * w.dv * w.dk * 4
+    paths = {
+        "one_pass": lambda: gdn.prefill_emit_checkpoints(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.ckpt_pos,
+                                                         flags=w.flags, ckpt_states=ck, state_out=st, o=o),
+        "split3": lambda: gdn.prefill_emit_checkpoints_split(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset,
+                                                             w.ckpt_pos, flags=w.flags, ckpt_states=ck,
+                                                             state_out=st, o=o, workspace=ws),
+    }
+    stream = torch.cuda.current_stream(dev)
+    for name, fn in paths.items():
+        for _ in range(max(args.warmup, 2)):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, min(args.steps, 10))
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        print(json.dumps({"metric": "prefill with checkpoint emission", "path": name, "ms": ms,
+                          "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_bytes": nbytes,
+                          "hbm_frac": nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                          "config": {"requests": w.B, "heads": w.H, "N": w.n_tokens[0], "checkpoints": M,
+                                     "d": w.dk, "inputs": "bf16"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +233,9 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="instead of the headline line, time the tail replay overlapped with a "
                          "host-to-device KV transfer on a second stream, one JSON line per KV size")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the headline line, time the prefill with emission (4 x 32 pairs, "
+                         "N = 65536, 16 checkpoints) in one pass and split in three segments")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -216,6 +256,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe_mib:
         copy_probe(torch, dev, args)
+        return
+    if args.prefill:
+        prefill_bench(torch, gdn, W.config(5, device=dev), dev, args)
         return
     w = W.config(3, device=dev)
     if args.overlap:
