@@ -258,9 +258,9 @@ def main():
         copy_probe(torch, dev, args)
         return
     if args.prefill:
-        prefill_bench(torch, gdn, W.config(5, device=dev), dev, args)
+        prefill_bench(torch, gdn, W.named("prefill_emit_B4_H32_N65536", device=dev), dev, args)
         return
-    w = W.config(3, device=dev)
+    w = W.named("tail5_B16_H32_m32768", device=dev)
     if args.overlap:
         overlap_bench(torch, gdn, w, dev)
         return

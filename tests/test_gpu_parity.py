@@ -117,12 +117,15 @@ def _sample_pairs(w, n, seed):
     return pairs
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_full_size_workloads(gdn, cfg):
-    w = W.config(cfg, device="cuda")
-    npairs = {2: 24, 3: 24, 5: 4}[cfg]
-    _check_workload(gdn, w, "auto", pairs=_sample_pairs(w, npairs, cfg), poison=(cfg == 2),
-                    label=f"config{cfg}")
+FULL_SIZE = {"resume_B8_H16_N8192": (24, 2), "tail5_B16_H32_m32768": (24, 3), "prefill_emit_B4_H32_N65536": (4, 5)}
+
+
+@pytest.mark.parametrize("name", list(FULL_SIZE))
+def test_full_size_workloads(gdn, name):
+    w = W.named(name, device="cuda")
+    npairs, seed = FULL_SIZE[name]
+    _check_workload(gdn, w, "auto", pairs=_sample_pairs(w, npairs, seed), poison=name.startswith("resume"),
+                    label=name)
 
 
 def test_grouped_tail_three_layers(gdn):
@@ -133,7 +136,7 @@ def test_grouped_tail_three_layers(gdn):
     GPU chain is also compared end to end as a diagnostic: after layer 1 the two
     chains read different bf16 inputs (rounding decisions on o differ), so that
     difference compounds and is only held to a loose 1e-2 bound."""
-    w = W.config(4, device="cuda")
+    w = W.named("tail10_grouped_B16_H32_m32768_L3", device="cuda")
     pairs = _sample_pairs(w, 8, 4)
     spans = PT.spans_of(w)
     alphas = [w.alpha] + list(w.layer_alpha)
@@ -370,7 +373,7 @@ def test_tail_replay_with_h2d_matches_plain(gdn, kernel):
 def test_tail_replay_with_h2d_overlaps(gdn):
     """[TR] §2.5 latency model: with the KV transfer on its own stream the two
     take about max(T_KV, T_replay), less than the serial sum."""
-    w = W.config(3, device="cuda")
+    w = W.named("tail5_B16_H32_m32768", device="cuda")
     st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
     o = torch.empty_like(w.v)
     n = 32 << 20
@@ -487,8 +490,8 @@ def test_split_prefill_parity(gdn, dtype, d):
 def test_split_prefill_full_size(gdn):
     """The prefill workload (4 x 32 pairs, N = 65536, 16 emissions) through the
     split path, on sampled pairs, and its time next to the one-pass prefill."""
-    w = W.config(5, device="cuda")
-    _split_check(gdn, w, "config5-split", pairs=_sample_pairs(w, 4, 5))
+    w = W.named("prefill_emit_B4_H32_N65536", device="cuda")
+    _split_check(gdn, w, "prefill64k-split", pairs=_sample_pairs(w, 4, 5))
     ws = torch.empty(gdn.prefill_split_workspace_bytes(w.B, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
     st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
     ck = torch.empty(w.B, len(w.ckpt_pos[0]), w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
@@ -514,7 +517,7 @@ def test_split_prefill_full_size(gdn):
         return a.elapsed_time(b) / 3
 
     t1, t3 = t(one), t(split)
-    _log(f"[config5-split] one pass {t1:.3f} ms, three segments {t3:.3f} ms")
+    _log(f"[prefill64k-split] one pass {t1:.3f} ms, three segments {t3:.3f} ms")
 
 
 # --- extreme gates and zero values -----------------------------------------------

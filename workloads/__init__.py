@@ -205,17 +205,17 @@ def poison_outside(w: Workload, spans) -> None:
         t[bad] = float("nan")
 
 
-# The five headline workloads, at their full sizes.
-def config(i: int, device="cpu"):
-    if i == 1:
-        return tiny_prefill(device=device)
-    if i == 2:
-        return resume(device=device)
-    if i == 3:
-        return tail(device=device)
-    if i == 4:
-        return tail(device=device, seed=4, r_num=10, r_den=100, layers=3,
-                    name="tail_grouped_B16_H32_m32768_r10_L3")
-    if i == 5:
-        return prefill(device=device)
-    raise ValueError(i)
+# The five headline workloads, at their full sizes, by name.
+WORKLOADS = {
+    "tiny_prefill_d16": lambda device: tiny_prefill(device=device),
+    "resume_B8_H16_N8192": lambda device: resume(device=device),
+    "tail5_B16_H32_m32768": lambda device: tail(device=device),
+    "tail10_grouped_B16_H32_m32768_L3": lambda device: tail(device=device, seed=4, r_num=10, r_den=100, layers=3,
+                                                             name="tail_grouped_B16_H32_m32768_r10_L3"),
+    "prefill_emit_B4_H32_N65536": lambda device: prefill(device=device),
+}
+
+
+def named(name: str, device="cpu"):
+    """One of the five headline workloads (WORKLOADS) at full size."""
+    return WORKLOADS[name](device)
