@@ -155,3 +155,22 @@ def test_split_prefill_workspace_checks(gdn):
     assert b"overlaps" in lib.gdn_last_error()
     sh2 = gdn._Shape(B=1, H=2, dk=128, dv=64, dtype=1, flags=0)
     assert call(0x900000000, 10 ** 9, shape=sh2) == 2
+
+
+def test_overlapped_replay_argument_errors(gdn):
+    """The transfer arguments are checked before anything is queued."""
+    lib = gdn.load()
+    sh = gdn._Shape(B=2, H=2, dk=128, dv=128, dtype=1, flags=1)
+    off = gdn._i64([0, 10, 20])
+    m = gdn._i64([10, 10])
+    p = ctypes.c_void_p(FAKE)
+
+    def call(dst, src, nbytes, event, r_den=100):
+        return lib.gdn_tail_replay_with_h2d(ctypes.byref(sh), p, p, p, p, p, gdn._p64(off), None, gdn._p64(m),
+                                            5, r_den, p, p, None, dst, src, nbytes, None, None, event)
+
+    assert call(FAKE, FAKE, 1024, None) == 1 and "copy_done" in lib.gdn_last_error().decode()
+    assert call(None, FAKE, 1024, FAKE) == 1 and "kv_dst" in lib.gdn_last_error().decode()
+    assert call(FAKE, None, 1024, FAKE) == 1
+    # replay arguments are validated first: nothing is queued on an invalid ratio
+    assert call(FAKE, FAKE, 1024, FAKE, r_den=0) == 1 and "ratio" in lib.gdn_last_error().decode()
