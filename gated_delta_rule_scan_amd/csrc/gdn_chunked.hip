@@ -136,10 +136,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Keeps the compiler from moving memory accesses across this point (LDS
-// reads above it stay issued early); no wait is implied.
-__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
-
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -424,13 +420,12 @@ __device__ __forceinline__ void load_kq(Pref &pf, uint32_t sm_lds, const Bases &
 // 16 k .. 16 k + 15, lane l taking row 16 k + l/4, value columns
 // 32 w + 8 (l%4) .. +7 (LDS: slice + 1 KiB k + 16 l).
 // sm_lds is the LDS byte address of the workgroup's Smem.
-template <int K0 = 0, int K1 = 2>
 __device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const Bases &G, int t0, int lc, int w,
                                       const Lane &L) {
     const uint64_t base = at_tok(G.v, t0, G.ts);
     const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.vldc;
 #pragma unroll
-    for (int k = K0; k < K1; ++k)
+    for (int k = 0; k < 2; ++k)
         dma16(base, min(L.vld[k], lim), sm_lds + OFF_VR + (uint32_t)(((vb * NW + w) * C * 32 + 16 * k * 32) * 2));
 }
 

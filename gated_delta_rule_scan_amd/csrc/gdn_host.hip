@@ -10,7 +10,14 @@
 //  - resume ("Sparse prefix caching for hybrid and recurrent LLM serving" §3):
 //    the deepest checkpoint c_j <= d (none: zero start), positions c_j + 1 .. d;
 //  - prefill with emission (same page, §3): positions 1 .. N from zero, the
-//    state after each checkpoint position is stored.
+//    state after each checkpoint position is stored;
+//  - the split prefill: the same in three segments per span, joined by the
+//    exact split of the Tail-Replay page §2.3 (S_end = S_start P + S^, with
+//    the transition product P scanned as v = 0 from the identity);
+//  - tail replay with a host-to-device transfer on a second stream (same
+//    page, §2.5).
+// Apart from the split prefill's caller-provided workspace, no device memory
+// beyond the caller's inputs and outputs is used.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>

@@ -1,8 +1,9 @@
 // Launch descriptor passed by value to every replay kernel, and the launcher
 // entry points shared by the host code and the kernel translation units.
 //
-// One launch covers up to kMaxReqPerLaunch requests.  Each request contributes
-// H x (d_v / DVB) workgroups, one per (request, head, block of DVB value rows).
+// One launch covers up to kMaxReqPerLaunch work items (a request's span, or
+// a segment of it in the split prefill).  Each item contributes H x (d_v / DVB)
+// workgroups, one per (item, head, block of DVB value rows).
 // The rows of the d_v x d_k state are independent of each other (the key
 // operator acts from the right, "Tail-Replay: Escaping the Curse of Linear
 // Attention in Prefix Caching for Hybrid LLMs" §2.3), so a (request, head)
