@@ -286,6 +286,7 @@ struct Lane {
     uint32_t cvt;       // conversion stores of row 4 b + lane/16, block b = 0 (krow)
     uint32_t st;        // transposed reads of T^T / P^T
     uint32_t vrd;       // transposed reads of the wave's V slice
+    uint32_t vrdr;      // the same reads from a raw key tile (q = k = v): row stride 256 bytes, wave w at +64 w
     uint32_t cwr;       // this wave's coefficient rows, lane half hi32
     uint32_t ld[2];     // global byte offsets of the key/query rows 8 w + 4 j + lane/16 (copy j)
     uint32_t ldc;       // column part of ld (16 bytes per lane of a row)
@@ -332,6 +333,7 @@ __device__ __forceinline__ Lane make_lane(int tid, int w, int H) {
     L.cvt = krow(g) * KROWB + 32 * (n >> 1) + 8 * (n & 1);
     L.st = 64 * (4 * (g >> 1) + (n >> 2)) + 2 * (16 * (g & 1) + 4 * (n & 3));
     L.vrd = 64 * (4 * (g >> 1) + (n >> 2)) + 32 * (g & 1) + 8 * (n & 3);
+    L.vrdr = 256 * (4 * (g >> 1) + (n >> 2)) + 64 * w + 32 * (g & 1) + 8 * (n & 3);
     L.cwr = OFF_CW + w * 4 * C * 4 + 16 * L.hi32;
     const uint32_t hdk2 = (uint32_t)(H * DK * 2);
     L.ldc = 16 * n;
@@ -398,13 +400,13 @@ __device__ __forceinline__ uint64_t at_tok(uint64_t base, int t0, uint32_t strid
 // WHICH = 0: keys; 1: queries (when COPY) and, from wave 1, the gates.
 template <int WHICH, bool COPY = true>
 __device__ __forceinline__ void load_kq(Pref &pf, uint32_t sm_lds, const Bases &G, int t0, int lc, int w,
-                                        const Lane &L) {
+                                        const Lane &L, uint32_t tile = OFF_KQR + WHICH * C * DK * 2) {
     const uint64_t base = at_tok(WHICH ? G.q : G.k, t0, G.ts);
     const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.ldc;
     if (COPY) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            dma16(base, min(L.ld[j], lim), sm_lds + OFF_KQR + (uint32_t)((WHICH * C + 8 * w + 4 * j) * DK * 2));
+            dma16(base, min(L.ld[j], lim), sm_lds + tile + (uint32_t)((8 * w + 4 * j) * DK * 2));
     }
     if (WHICH == 1 && w == 1) {
         typedef __attribute__((address_space(1))) const uint16_t gu16;
@@ -431,7 +433,8 @@ __device__ __forceinline__ void dma_v(uint32_t sm_lds, int vb, const Bases &G, i
 
 // Wave 3 copies the key rows and the V columns of all four waves (the other
 // waves carry the longer tile tasks in the same phase).
-__device__ __forceinline__ void load_k_all(uint32_t sm_lds, const Bases &G, int t0, int lc, const Lane &L) {
+__device__ __forceinline__ void load_k_all(uint32_t sm_lds, const Bases &G, int t0, int lc, const Lane &L,
+                                           uint32_t tile = OFF_KQR) {
     const uint64_t base = at_tok(G.k, t0, G.ts);
     const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.ldc;
 #pragma unroll
@@ -439,7 +442,7 @@ __device__ __forceinline__ void load_k_all(uint32_t sm_lds, const Bases &G, int 
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             dma16(base, min(L.ld[j] - (uint32_t)(8 * (3 - w2)) * G.ts, lim),
-                  sm_lds + OFF_KQR + (uint32_t)((8 * w2 + 4 * j) * DK * 2));
+                  sm_lds + tile + (uint32_t)((8 * w2 + 4 * j) * DK * 2));
 }
 __device__ __forceinline__ void dma_v_all(uint32_t sm_lds, int vb, const Bases &G, int t0, int lc, const Lane &L) {
     const uint64_t base3 = at_tok(G.v, t0, G.ts);  // G.v holds wave 3's columns
@@ -508,7 +511,8 @@ __device__ constexpr int cvt_owner(int gi) {  // gi: block gi/2 of keys (gi even
 }
 
 template <bool WANT_Q, bool NORM_Q, int W>
-__device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &pf, int lc, const Lane &L) {
+__device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &pf, int lc, const Lane &L,
+                                                 uint32_t rawk = OFF_KQR, uint32_t rawq = OFF_KQR + C * DK * 2) {
     const uint32_t kbuf = OFF_KH + pb * KBUF, qbuf = OFF_QH + pb * KBUF;
     constexpr int NG = WANT_Q ? 16 : 8;
 #pragma unroll
@@ -518,7 +522,7 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
         const int rb = WANT_Q ? (gi >> 1) : gi;
         const int t = 4 * rb + L.g;
         const bool live = t < lc;
-        const uint32_t raw = OFF_KQR + (uint32_t)(kind * C * DK * 2 + rb * 4 * DK * 2) + 16 * L.lane;
+        const uint32_t raw = (kind ? rawq : rawk) + (uint32_t)(rb * 4 * DK * 2) + 16 * L.lane;
         const uint32_t dst = (kind ? qbuf : kbuf) + L.cvt + (uint32_t)(((rb & 3) + 16 * (rb >> 2)) * KROWB);
         if (kind == 0) {
             convert_row<true>(sm, dst, lds_ld<uint4>(sm, raw), live, nullptr);
@@ -770,7 +774,7 @@ __device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, gchar *ob
 // One wave's part of a (request, head).  ROLE is the wave index: it selects
 // the wave's value rows and key-side task, and as a compile-time constant it
 // removes the per-chunk role branches.
-template <int ROLE, bool WANT_O, bool NORM_Q>
+template <int ROLE, bool WANT_O, bool NORM_Q, bool ALIAS>
 __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_t sm_lds)
 {
 
@@ -875,24 +879,30 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     Chunk nx = next_chunk(P, cur, len, ne_end);
     Pref pf;
     int vb = 0;  // V buffer of the current chunk
+    // With q = k = v (ALIAS) a chunk's rows are copied once, into raw tile
+    // (chunk index % 2), and serve as keys, queries and values until the
+    // copy of the chunk two ahead replaces them.
+    constexpr uint32_t RAW1 = OFF_KQR + C * DK * 2;  // second raw tile
     if (cur.lc > 0) {
-        if (!zero_v) dma_v(sm_lds, 0, G, cur.t0, cur.lc, w, L);
+        if (!zero_v && !ALIAS) dma_v(sm_lds, 0, G, cur.t0, cur.lc, w, L);
         load_kq<0>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
-        load_kq<1, WANT_O>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
+        load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the raw rows of chunk 0 have landed (each wave its own copies)
     }
     lds_barrier();
     if (cur.lc > 0) {
-        key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
-        lds_barrier();  // the raw tiles are free again
+        if (ALIAS) key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L, OFF_KQR, OFF_KQR);
+        else key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
+        lds_barrier();  // the raw tiles are free again (ALIAS: tile 0 keeps chunk 0's values)
         if (nx.lc > 0) {
-            load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
-            load_kq<1, WANT_O>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
+            load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L, ALIAS ? RAW1 : OFF_KQR);
+            load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
         }
         key_side_tasks<WANT_O>(sm, 0, w, L);
     }
 
-    int p = 0;  // key-side buffer of the current chunk
+    int p = 0;   // key-side buffer of the current chunk
+    int kp = 0;  // ALIAS: raw tile of the current chunk
     // outputs of the previous chunk, staged in V buffer vb_pend, are stored after the next barrier
     gchar *obase_pend = nullptr;
     int lc_pend = 0, vb_pend = 0;
@@ -913,7 +923,14 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         float *cwl = sm.cw[w][0];
 
         // key side of `nx`: conversion (independent of the state chain above)
-        if (nx.lc > 0) key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
+        if (nx.lc > 0) {
+            if (ALIAS) {
+                const uint32_t rawn = kp ? OFF_KQR : RAW1;  // raw tile of `nx`
+                key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L, rawn, rawn);
+            } else {
+                key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
+            }
+        }
         // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
         // (all fragments are read first, so that the reads overlap)
         half8 kf[8], qf[8];
@@ -951,12 +968,17 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
         float bm = 0.f;
         {
-            const uint32_t vbase = OFF_VR + (uint32_t)((vb * NW + w) * C * 32 * 2) + L.vrd;
+            // values: the wave's V slice (64-byte token rows), or with ALIAS the
+            // raw tile of `cur` (256-byte rows); zero-v works keep the zeroed slices
+            const bool rawv = ALIAS && !zero_v;
+            const uint32_t vbase = rawv ? (kp ? RAW1 : OFF_KQR) + L.vrdr
+                                        : OFF_VR + (uint32_t)((vb * NW + w) * C * 32 * 2) + L.vrd;
+            const uint32_t vstep = rawv ? 8 * DK * 2 : 512;  // 8 tokens
             i16x4_t vv[4];
             float4 c4[4];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                vv[q4] = tr4u(sm, vbase + 512 * q4);
+                vv[q4] = tr4u(sm, vbase + vstep * q4);
                 c4[q4] = lds_ld<float4>(sm, cw + 32 * q4);
             }
 #pragma unroll
@@ -990,15 +1012,15 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         const bool has2 = nx2.lc > 0;
         const int kt2 = has2 ? nx2.t0 : cur.t0;
         const int klc2 = has2 ? nx2.lc : cur.lc;
-        if (w == 3) load_k_all(sm_lds, G, kt2, klc2, L);
+        if (w == 3) load_k_all(sm_lds, G, kt2, klc2, L, ALIAS ? (kp ? RAW1 : OFF_KQR) : OFF_KQR);
         // V of `nx` into the other V buffer (its staged outputs went out after the
         // first barrier; without a next chunk, rows of `cur` are copied and ignored)
-        if (!zero_v && w == 3) {
+        if (!zero_v && !ALIAS && w == 3) {
             const bool has1 = nx.lc > 0;
             dma_v_all(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L);
         }
         if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
-        load_kq<1, WANT_O>(pf, sm_lds, G, kt2, klc2, w, L);
+        load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
 
         // U = (T diag(beta)) B~
         floatx16 U = {};
@@ -1131,6 +1153,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         nx = nx2;
         p ^= 1;
         vb ^= 1;
+        kp ^= 1;
     }
 
     if (WANT_O && lc_pend > 0) {
@@ -1140,16 +1163,16 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     if (P.state_dst[r]) store_state(P.state_dst[r] + (int64_t)h * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
-template <bool WANT_O, bool NORM_Q>
+template <bool WANT_O, bool NORM_Q, bool ALIAS>
 __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 {
     __shared__ Smem sm;
     const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-        case 0: wave_main<0, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 1: wave_main<1, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 2: wave_main<2, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        default: wave_main<3, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 0: wave_main<0, WANT_O, NORM_Q, ALIAS>(P, sm, sm_lds); break;
+        case 1: wave_main<1, WANT_O, NORM_Q, ALIAS>(P, sm, sm_lds); break;
+        case 2: wave_main<2, WANT_O, NORM_Q, ALIAS>(P, sm, sm_lds); break;
+        default: wave_main<3, WANT_O, NORM_Q, ALIAS>(P, sm, sm_lds); break;
     }
 }
 
@@ -1163,15 +1186,19 @@ hipError_t launch_chunked(const LaunchDesc &d, int dk, int dv, Elem e, hipStream
     if (!chunked_supported(dk, dv, e)) return hipErrorNotSupported;
     const int nwg = d.nreq * d.H;
     if (nwg == 0) return hipSuccess;
-    const bool want_o = d.o != nullptr, norm_q = (d.flags & kNormQ) != 0;
-    if (want_o && norm_q)
-        hipLaunchKernelGGL((chunked_kernel<true, true>), dim3(nwg), dim3(NT), 0, s, d);
-    else if (want_o)
-        hipLaunchKernelGGL((chunked_kernel<true, false>), dim3(nwg), dim3(NT), 0, s, d);
-    else if (norm_q)
-        hipLaunchKernelGGL((chunked_kernel<false, true>), dim3(nwg), dim3(NT), 0, s, d);
-    else
-        hipLaunchKernelGGL((chunked_kernel<false, false>), dim3(nwg), dim3(NT), 0, s, d);
+    const bool want_o = d.o != nullptr, norm_q = (d.flags & kNormQ) != 0, alias = (d.flags & kAliasQKV) != 0;
+    const dim3 grid(nwg), block(NT);
+    if (alias) {
+        if (want_o && norm_q) hipLaunchKernelGGL((chunked_kernel<true, true, true>), grid, block, 0, s, d);
+        else if (want_o) hipLaunchKernelGGL((chunked_kernel<true, false, true>), grid, block, 0, s, d);
+        else if (norm_q) hipLaunchKernelGGL((chunked_kernel<false, true, true>), grid, block, 0, s, d);
+        else hipLaunchKernelGGL((chunked_kernel<false, false, true>), grid, block, 0, s, d);
+    } else {
+        if (want_o && norm_q) hipLaunchKernelGGL((chunked_kernel<true, true, false>), grid, block, 0, s, d);
+        else if (want_o) hipLaunchKernelGGL((chunked_kernel<true, false, false>), grid, block, 0, s, d);
+        else if (norm_q) hipLaunchKernelGGL((chunked_kernel<false, true, false>), grid, block, 0, s, d);
+        else hipLaunchKernelGGL((chunked_kernel<false, false, false>), grid, block, 0, s, d);
+    }
     return hipGetLastError();
 }
 

@@ -200,6 +200,9 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
     d.emit_base = emit_base;
     d.H = s->H;
     d.flags = (int32_t)(s->flags & (GDN_NORMALIZE_K | GDN_NORMALIZE_Q));
+    // one tensor for q, k and v (a layer fed its predecessor's outputs): the
+    // chunked kernel then reads each row once
+    if (chunked && k && k == v && s->dk == s->dv && (!o || q == k)) d.flags |= gdn::kAliasQKV;
     d.M = M;
 
     size_t i = 0;

@@ -47,6 +47,9 @@ static_assert(sizeof(LaunchDesc) <= 3584, "descriptor must fit the kernel argume
 // Flags mirrored from the public header (kept numerically identical).
 constexpr int kNormK = 1;
 constexpr int kNormQ = 2;
+// LaunchDesc::flags bit set by the host (not a public flag): q, k and v are
+// one tensor (d_k = d_v), so each row is read once and serves all three.
+constexpr int kAliasQKV = 1 << 16;
 
 // Per-work flags (LaunchDesc::wflags).  The sequence-split prefill runs, for a
 // middle segment of a span, the zero-start scan (kWorkNoOut) and the product
