@@ -213,6 +213,98 @@ def prefill_bench(torch, gdn, w, dev, args):
                                      "d": w.dk, "inputs": "bf16"}}), flush=True)
 
 
+def workloads_bench(torch, gdn, W, dev, args):
+    """Every headline workload at full size through the library, timed with HIP
+    events on the launch stream (median of 5 timed batches after warm-up)."""
+    import numpy as np
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps=10):
+        # warm-up for a fixed wall time, until the GPU clocks have settled
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < max(args.device_warmup_s, 0.3):
+            fn()
+            torch.cuda.synchronize()
+        out = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / reps)
+        return float(np.median(out))
+
+    def line(name, ms, tokens, nbytes, extra=None):
+        d = {"metric": "workload time", "workload": name, "ms": ms, "replayed_tokens": tokens,
+             "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_bytes": nbytes,
+             "hbm_frac": nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+        d.update(extra or {})
+        print(json.dumps(d), flush=True)
+
+    # resume: 8 x 16 pairs, prefix 8192, 8 balanced checkpoints, depths ~ U{1..N}
+    w = W.named("resume_B8_H16_N8192", device=dev)
+    st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    o = torch.empty_like(w.v)
+    js = [0] * w.B
+    spans = []
+    for b in range(w.B):
+        j = gdn.select_checkpoint(w.ckpt_pos[b], w.depth[b])
+        c = 0 if j == 0 else w.ckpt_pos[b][j - 1]
+        spans.append(w.depth[b] - c)
+        js[b] = j
+    toks = sum(spans)
+    nb = algorithmic_bytes(toks * w.H, w.B * w.H, w.dk, w.dv, 2) + sum(1 for j in js if j > 0) * w.H * w.dv * w.dk * 4
+    ms = timed(lambda: gdn.resume(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.ckpt_pos, w.ckpt_states,
+                                  w.depth, first_pos=w.first_pos, flags=w.flags, state_out=st, o=o))
+    line(w.name, ms, toks, nb, {"mean_span": toks / w.B})
+    # tail 5%
+    w = W.named("tail5_B16_H32_m32768", device=dev)
+    st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    o = torch.empty_like(w.v)
+    ks = [gdn.tail_len(m, w.r_num, w.r_den) for m in w.m]
+    ms = timed(lambda: gdn.tail_replay(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m, w.r_num, w.r_den,
+                                       first_pos=w.first_pos, flags=w.flags, state_out=st, o=o))
+    line(w.name, ms, sum(ks), algorithmic_bytes(sum(ks) * w.H, w.B * w.H, w.dk, w.dv, 2))
+    # grouped tail 10%, three layers: layer l+1 reads layer l's outputs as q = k = v
+    w = W.named("tail10_grouped_B16_H32_m32768_L3", device=dev)
+    ks = [gdn.tail_len(m, w.r_num, w.r_den) for m in w.m]
+    alphas = [w.alpha] + list(w.layer_alpha)
+    betas = [w.beta] + list(w.layer_beta)
+    st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    outs = [torch.empty_like(w.v) for _ in range(3)]
+
+    def group():
+        q, k, v = w.q, w.k, w.v
+        for layer in range(3):
+            gdn.tail_replay(q, k, v, alphas[layer], betas[layer], w.tok_offset, w.m, w.r_num, w.r_den,
+                            first_pos=w.first_pos, flags=w.flags, state_out=st, o=outs[layer])
+            q = k = v = outs[layer]
+    th = sum(ks) * w.H
+    # layer 1 reads q, k, v; layers 2 and 3 read one tensor; each layer writes o and its states
+    nb = (algorithmic_bytes(th, w.B * w.H, w.dk, w.dv, 2)
+          + 2 * (th * (2 * w.dk + 2 * 2 + 2 * w.dv) + w.B * w.H * w.dv * w.dk * 4))
+    ms = timed(group, reps=5)
+    line(w.name, ms, sum(ks), nb, {"layers": 3, "tokens_are_per_layer": True})
+    # prefill with emission, one pass and split
+    w = W.named("prefill_emit_B4_H32_N65536", device=dev)
+    M = len(w.ckpt_pos[0])
+    st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    ck = torch.empty(w.B, M, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    o = torch.empty_like(w.v)
+    ws = torch.empty(gdn.prefill_split_workspace_bytes(w.B, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    toks = sum(w.n_tokens)
+    nb = algorithmic_bytes(toks * w.H, w.B * w.H, w.dk, w.dv, 2) + w.B * M * w.H * w.dv * w.dk * 4
+    ms = timed(lambda: gdn.prefill_emit_checkpoints(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.ckpt_pos,
+                                                    flags=w.flags, ckpt_states=ck, state_out=st, o=o), reps=3)
+    line(w.name, ms, toks, nb, {"path": "one pass"})
+    ms = timed(lambda: gdn.prefill_emit_checkpoints_split(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset,
+                                                          w.ckpt_pos, flags=w.flags, ckpt_states=ck, state_out=st,
+                                                          o=o, workspace=ws), reps=3)
+    line(w.name, ms, toks, nb, {"path": "three segments"})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +328,10 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the headline line, time the prefill with emission (4 x 32 pairs, "
                          "N = 65536, 16 checkpoints) in one pass and split in three segments")
+    ap.add_argument("--workloads", action="store_true",
+                    help="instead of the headline line, print one line per headline workload (resume, "
+                         "tail 5%%, grouped tail 10%% over three layers, prefill with emission): "
+                         "HIP-event time per call, algorithmic bytes and the fraction of the HBM peak")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -256,6 +352,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe_mib:
         copy_probe(torch, dev, args)
+        return
+    if args.workloads:
+        workloads_bench(torch, gdn, W, dev, args)
         return
     if args.prefill:
         prefill_bench(torch, gdn, W.named("prefill_emit_B4_H32_N65536", device=dev), dev, args)
