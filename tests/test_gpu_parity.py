@@ -626,3 +626,19 @@ def test_aliased_grouped_layers_time(gdn):
     ta = t(lambda: call(x, x, x))
     ts = t(lambda: call(*xs))
     _log(f"[alias-time] grouped layer (16 x 32 pairs, 3277 tokens): aliased {ta:.3f} ms, separate {ts:.3f} ms")
+
+
+# --- chunk boundaries ------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+def test_chunk_boundary_spans(gdn, kernel):
+    """Spans of C - 1, C, C + 1, 2C - 1, 2C and 2C + 1 tokens (C = 32, the chunk
+    of the matrix-core kernel) resumed from a checkpoint at 100, and emissions
+    at positions c with c mod C in {0, 1, C - 1} around them."""
+    w = W.resume(seed=73, B=6, H=2, d=128, N=300, M=2, dtype="bf16",
+                 depths=[131, 132, 133, 163, 164, 165])
+    w.ckpt_pos = [[100, 200]] * 6
+    _check_workload(gdn, w, kernel, label="boundary-resume")
+    wp = W.prefill(seed=74, B=3, H=2, d=128, N=97, M=5, dtype="bf16", lengths=[31, 65, 97],
+                   positions=[[1, 2, 29, 30, 31], [1, 31, 32, 33, 65], [31, 32, 33, 64, 96]])
+    _check_workload(gdn, wp, kernel, label="boundary-prefill")
