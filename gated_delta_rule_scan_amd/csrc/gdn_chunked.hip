@@ -995,7 +995,13 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         int eB = 0;
         if (out_of_band(bm)) eB = f16_adjust(wave_max(bm));
         if (eB != 0) Y *= ldexpf(1.f, eB);
-        if (w == 3) key_side_combine(sm, p, L);
+        if (w == 3) {
+            // the last T step is on the critical path of this phase: it takes
+            // issue priority over the co-resident workgroup's waves
+            __builtin_amdgcn_s_setprio(2);
+            key_side_combine(sm, p, L);
+            __builtin_amdgcn_s_setprio(0);
+        }
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
         // operands of `cur` that are complete now are read before the tasks
         const half8 tfr0 = tr_frag_st(sm, OFF_TT, 0, L);
@@ -1019,7 +1025,9 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             const bool has1 = nx.lc > 0;
             dma_v_all(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L);
         }
+        if (w != 3) __builtin_amdgcn_s_setprio(1);  // the longer tasks of this phase go first
         if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
+        if (w != 3) __builtin_amdgcn_s_setprio(0);
         load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
 
         // U = (T diag(beta)) B~
