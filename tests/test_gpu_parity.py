@@ -642,3 +642,19 @@ def test_chunk_boundary_spans(gdn, kernel):
     wp = W.prefill(seed=74, B=3, H=2, d=128, N=97, M=5, dtype="bf16", lengths=[31, 65, 97],
                    positions=[[1, 2, 29, 30, 31], [1, 31, 32, 33, 65], [31, 32, 33, 64, 96]])
     _check_workload(gdn, wp, kernel, label="boundary-prefill")
+
+
+# --- queries used as given (no GDN_NORMALIZE_Q) ---------------------------------
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+@pytest.mark.parametrize("op", ["tail", "resume", "prefill"])
+def test_unnormalised_queries(gdn, kernel, op):
+    """Without GDN_NORMALIZE_Q the queries enter o = S q as stored; their norms
+    here span 1e-3 .. 1e3 per token (the chunked kernel scales each query row by
+    a power of two into the fp16 range and undoes it on the output)."""
+    w = _small(op, "bf16", 128, 128, seed=79)
+    g = torch.Generator().manual_seed(79)
+    scale = torch.exp(torch.empty(w.rows, w.H, 1).uniform_(-6.9, 6.9, generator=g))
+    w.q = (w.q.float() * scale).to(w.q.dtype)
+    w.flags = W.NORMALIZE_K
+    _check_workload(gdn, w, kernel, label=f"rawq-{op}")
