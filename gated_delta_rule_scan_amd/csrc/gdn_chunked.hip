@@ -515,6 +515,16 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
                                                  uint32_t rawk = OFF_KQR, uint32_t rawq = OFF_KQR + C * DK * 2) {
     const uint32_t kbuf = OFF_KH + pb * KBUF, qbuf = OFF_QH + pb * KBUF;
     constexpr int NG = WANT_Q ? 16 : 8;
+    // all raw rows of this wave are read before the first converted row is
+    // stored, so that the reads overlap instead of each waiting behind a store
+    uint4 raw[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        if (cvt_owner<WANT_Q>(gi) != W) continue;
+        const int kind = WANT_Q ? (gi & 1) : 0;
+        const int rb = WANT_Q ? (gi >> 1) : gi;
+        raw[gi] = lds_ld<uint4>(sm, (kind ? rawq : rawk) + (uint32_t)(rb * 4 * DK * 2) + 16 * L.lane);
+    }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         if (cvt_owner<WANT_Q>(gi) != W) continue;
@@ -522,13 +532,12 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
         const int rb = WANT_Q ? (gi >> 1) : gi;
         const int t = 4 * rb + L.g;
         const bool live = t < lc;
-        const uint32_t raw = (kind ? rawq : rawk) + (uint32_t)(rb * 4 * DK * 2) + 16 * L.lane;
         const uint32_t dst = (kind ? qbuf : kbuf) + L.cvt + (uint32_t)(((rb & 3) + 16 * (rb >> 2)) * KROWB);
         if (kind == 0) {
-            convert_row<true>(sm, dst, lds_ld<uint4>(sm, raw), live, nullptr);
+            convert_row<true>(sm, dst, raw[gi], live, nullptr);
         } else {
             float kqv = 1.f;
-            convert_row<NORM_Q>(sm, dst, lds_ld<uint4>(sm, raw), live, &kqv);
+            convert_row<NORM_Q>(sm, dst, raw[gi], live, &kqv);
             if (!NORM_Q && L.n16 == 0) sm.kq[pb][t] = kqv;
         }
     }
