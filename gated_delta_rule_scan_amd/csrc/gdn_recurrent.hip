@@ -11,8 +11,17 @@
 // Work split: one workgroup per (request, head, block of DVB value rows),
 // 4 lanes per row, each lane holding d_k/4 state elements in VGPRs.  Token
 // inputs are staged through LDS in blocks of TB tokens (converted to float32
-// there); the key/query norms are computed once per token in LDS; outputs of a
-// block are gathered in LDS and written back as contiguous rows.
+// there, 16 lanes per token, which also sum the squares for the key/query
+// norms); outputs of a block are gathered in LDS and written back as
+// contiguous rows.
+//
+// Per token t one pass over the state forms both S_{t-1} k_t and the previous
+// token's output S_{t-1} q_{t-1} (two independent dot products per lane, summed
+// over the 4 lanes of a row by DPP), and a second pass applies the rank-1
+// update with the key held in registers.  The decay is kept as a running
+// scalar: S = c R, so that a token costs one FMA per state element instead of
+// a multiply and an FMA; c is folded back into R at the end of each block, or
+// at once if it falls below 2^-30 (bounding 1/c).
 #include "gdn_launch.h"
 #include "gdn_numeric.h"
 
@@ -20,20 +29,44 @@ namespace gdn {
 namespace {
 
 constexpr int kLanesPerRow = 4;
-constexpr int kTB = 32;  // tokens staged per block
+constexpr int kTB = 16;   // tokens staged per block
+constexpr int kPPT = 16;  // staging lanes per token
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+// Sum over the 4 lanes of a quad (every lane receives it).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_f<0xB1>(x);  // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);  // quad_perm [2,3,0,1]
+    return x;
+}
+// Sum over 16 aligned lanes (every lane receives it).
+__device__ __forceinline__ float row16_sum(float x) {
+    x = quad_sum(x);
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    x += dpp_f<0x140>(x);  // row_mirror
+    return x;
+}
 
 template <int DK, int DV, int DVB, typename T>
-__global__ __launch_bounds__(kLanesPerRow * DVB)
+__global__ __launch_bounds__(kLanesPerRow * DVB, 4)  // four waves per SIMD
 void recurrent_kernel(const LaunchDesc P)
 {
     constexpr int NT = kLanesPerRow * DVB;
     constexpr int E = DK / kLanesPerRow;       // state elements per lane
     constexpr int E4 = E / 4;                  // float4 groups per lane
     constexpr int NBLK = DV / DVB;
-    static_assert(E % 4 == 0, "d_k must be a multiple of 16");
+    constexpr int CPT = DK / kPPT;             // staged columns per lane and token
+    // key/query row stride = 16 (mod 64) words, so that the four tokens staged
+    // by one wave land on different banks
+    constexpr int SK = DK + ((16 - DK) & 63);
+    static_assert(E % 4 == 0 && CPT >= 1, "d_k must be a multiple of 16");
+    static_assert((kTB * kPPT) % NT == 0 || NT % (kTB * kPPT) == 0, "staging lanes cover whole waves");
 
-    __shared__ float sk[kTB][DK];
-    __shared__ float sq[kTB][DK];
+    __shared__ __attribute__((aligned(16))) float sk[kTB][SK];
+    __shared__ __attribute__((aligned(16))) float sq[kTB][SK];
     __shared__ float sv[kTB][DVB];
     __shared__ float so[kTB][DVB];
     __shared__ float sa[kTB], sb[kTB], skn[kTB], sqn[kTB];
@@ -50,26 +83,29 @@ void recurrent_kernel(const LaunchDesc P)
     const int wf = P.wflags[r];
     const bool want_o = P.o != nullptr && !(wf & kWorkNoOut);
     const bool zero_v = (wf & kWorkZeroV) != 0;
+    const bool norm_k = (P.flags & kNormK) != 0, norm_q = (P.flags & kNormQ) != 0;
     const int H = P.H;
 
     // Lane `sub` owns key columns (g*4 + sub)*4 .. +3 for g in [0, E4): four
     // neighbouring lanes read 64 contiguous bytes per step (no bank conflicts).
-    float4 S[E4];
+    // The state is S = c R.
+    float4 R[E4];
+    float c = 1.f;
     if (wf & kWorkIdentity) {
 #pragma unroll
         for (int g = 0; g < E4; ++g) {
             const int c0 = (g * kLanesPerRow + sub) * 4;
-            S[g] = make_float4(c0 == grow ? 1.f : 0.f, c0 + 1 == grow ? 1.f : 0.f, c0 + 2 == grow ? 1.f : 0.f,
+            R[g] = make_float4(c0 == grow ? 1.f : 0.f, c0 + 1 == grow ? 1.f : 0.f, c0 + 2 == grow ? 1.f : 0.f,
                                c0 + 3 == grow ? 1.f : 0.f);
         }
     } else if (P.init_off[r] >= 0) {
         const float *src = P.init_base + P.init_off[r] + (int64_t)h * DV * DK + (int64_t)grow * DK;
 #pragma unroll
         for (int g = 0; g < E4; ++g)
-            S[g] = *reinterpret_cast<const float4 *>(src + (g * kLanesPerRow + sub) * 4);
+            R[g] = *reinterpret_cast<const float4 *>(src + (g * kLanesPerRow + sub) * 4);
     } else {
 #pragma unroll
-        for (int g = 0; g < E4; ++g) S[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int g = 0; g < E4; ++g) R[g] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
     const int len = P.len[r];
@@ -83,18 +119,77 @@ void recurrent_kernel(const LaunchDesc P)
     const T *bg = static_cast<const T *>(P.beta);
     T *og = static_cast<T *>(P.o);
 
+    // R . x over a lane's columns, two accumulators
+    auto dot = [&](const float4 (&x)[E4]) {
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int g = 0; g < E4; ++g) {
+            d0 = fmaf(R[g].x, x[g].x, d0);
+            d1 = fmaf(R[g].y, x[g].y, d1);
+            d0 = fmaf(R[g].z, x[g].z, d0);
+            d1 = fmaf(R[g].w, x[g].w, d1);
+        }
+        return d0 + d1;
+    };
+    // R . (row of LDS), the row read one group at a time
+    auto dot_lds = [&](const float *row) {
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int g = 0; g < E4; ++g) {
+            const float4 x = *reinterpret_cast<const float4 *>(row + (g * kLanesPerRow + sub) * 4);
+            d0 = fmaf(R[g].x, x.x, d0);
+            d1 = fmaf(R[g].y, x.y, d1);
+            d0 = fmaf(R[g].z, x.z, d0);
+            d1 = fmaf(R[g].w, x.w, d1);
+        }
+        return d0 + d1;
+    };
+    auto load_row = [&](const float *row, float4 (&x)[E4]) {
+#pragma unroll
+        for (int g = 0; g < E4; ++g) x[g] = *reinterpret_cast<const float4 *>(row + (g * kLanesPerRow + sub) * 4);
+    };
+    auto store_scaled = [&](float *dst, float sc) {
+#pragma unroll
+        for (int g = 0; g < E4; ++g) {
+            const float4 x = R[g];
+            *reinterpret_cast<float4 *>(dst + (g * kLanesPerRow + sub) * 4) =
+                make_float4(x.x * sc, x.y * sc, x.z * sc, x.w * sc);
+        }
+    };
+
     for (int t0 = 0; t0 < len; t0 += kTB) {
         const int nt = min(kTB, len - t0);
         __syncthreads();
-        for (int idx = tid; idx < nt * DK; idx += NT) {
-            const int t = idx / DK, j = idx % DK;
-            const int64_t base = ((row0 + t0 + t) * H + h) * DK + j;
-            sk[t][j] = to_f32(kg[base]);
-            if (want_o) sq[t][j] = to_f32(qg[base]);
+        // keys and queries: lanes 16 t .. 16 t + 15 of the staging pass convert
+        // token t (columns part, part + 16, ...) and sum its squares
+        for (int idx = tid; idx < kTB * kPPT; idx += NT) {
+            const int t = idx / kPPT, part = idx % kPPT;
+            float kk = 0.f, qq = 0.f;
+            if (t < nt) {
+                const int64_t base = ((row0 + t0 + t) * H + h) * DK;
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    const int j = part + kPPT * i;
+                    const float x = to_f32(kg[base + j]);
+                    sk[t][j] = x;
+                    kk = fmaf(x, x, kk);
+                    if (want_o) {
+                        const float y = to_f32(qg[base + j]);
+                        sq[t][j] = y;
+                        qq = fmaf(y, y, qq);
+                    }
+                }
+            }
+            kk = row16_sum(kk);
+            qq = row16_sum(qq);
+            if (part == 0 && t < nt) {
+                skn[t] = norm_k ? inv_norm(kk) : 1.f;
+                sqn[t] = norm_q ? inv_norm(qq) : 1.f;
+            }
         }
         for (int idx = tid; idx < nt * DVB; idx += NT) {
-            const int t = idx / DVB, c = idx % DVB;
-            sv[t][c] = zero_v ? 0.f : to_f32(vg[((row0 + t0 + t) * H + h) * DV + blk * DVB + c]);
+            const int t = idx / DVB, cc = idx % DVB;
+            sv[t][cc] = zero_v ? 0.f : to_f32(vg[((row0 + t0 + t) * H + h) * DV + blk * DVB + cc]);
         }
         if (tid < nt) {
             const int64_t ab = (row0 + t0 + tid) * H + h;
@@ -102,74 +197,73 @@ void recurrent_kernel(const LaunchDesc P)
             sb[tid] = to_f32(bg[ab]);
         }
         __syncthreads();
-        if (tid < nt) {
-            float kk = 0.f, qq = 0.f;
-            for (int j = 0; j < DK; ++j) {
-                kk += sk[tid][j] * sk[tid][j];
-                if (want_o) qq += sq[tid][j] * sq[tid][j];
-            }
-            skn[tid] = (P.flags & kNormK) ? inv_norm(kk) : 1.f;
-            sqn[tid] = (P.flags & kNormQ) ? inv_norm(qq) : 1.f;
-        }
-        __syncthreads();
 
         for (int t = 0; t < nt; ++t) {
-            const float a = sa[t];
-            const float kn = skn[t];
-            float u = 0.f;
-#pragma unroll
-            for (int g = 0; g < E4; ++g) {
-                const float4 kv = *reinterpret_cast<const float4 *>(&sk[t][(g * kLanesPerRow + sub) * 4]);
-                u += S[g].x * kv.x + S[g].y * kv.y + S[g].z * kv.z + S[g].w * kv.w;
+            float4 kv[E4];
+            load_row(sk[t], kv);
+            float u;
+            if (want_o && t > 0) {
+                // the output of token t - 1 comes from the same state S_{t-1}
+                u = dot(kv);
+                const float p = quad_sum(dot_lds(sq[t - 1]));
+                if (sub == 0) so[t - 1][lrow] = p * c * sqn[t - 1];
+            } else {
+                u = dot(kv);
             }
-            u += __shfl_xor(u, 1);
-            u += __shfl_xor(u, 2);
-            // w multiplies the raw key, so it carries the norm factor twice:
-            // beta (v - alpha S k^) k^^T with k^ = kn * k.
-            const float w = sb[t] * (sv[t][lrow] - a * (u * kn)) * kn;
-#pragma unroll
-            for (int g = 0; g < E4; ++g) {
-                const float4 kv = *reinterpret_cast<const float4 *>(&sk[t][(g * kLanesPerRow + sub) * 4]);
-                S[g].x = fmaf(w, kv.x, a * S[g].x);
-                S[g].y = fmaf(w, kv.y, a * S[g].y);
-                S[g].z = fmaf(w, kv.z, a * S[g].z);
-                S[g].w = fmaf(w, kv.w, a * S[g].w);
-            }
-            if (want_o) {
-                float p = 0.f;
+            u = quad_sum(u);
+            const float a = sa[t], kn = skn[t];
+            const float ut = c * kn * u;  // S_{t-1} k^_t
+            float cn = c * a;
+            if (cn < 0x1p-30f) {
+                // apply the decay now, so that 1/c stays bounded
 #pragma unroll
                 for (int g = 0; g < E4; ++g) {
-                    const float4 qv = *reinterpret_cast<const float4 *>(&sq[t][(g * kLanesPerRow + sub) * 4]);
-                    p += S[g].x * qv.x + S[g].y * qv.y + S[g].z * qv.z + S[g].w * qv.w;
+                    R[g].x *= cn;
+                    R[g].y *= cn;
+                    R[g].z *= cn;
+                    R[g].w *= cn;
                 }
-                p += __shfl_xor(p, 1);
-                p += __shfl_xor(p, 2);
-                if (sub == 0) so[t][lrow] = p * sqn[t];
+                cn = 1.f;
             }
-            if (ne < ne_end && P.emit_after[ne] == t0 + t + 1) {
-                float *dst = P.emit_base +
-                    ((((int64_t)b * P.M + P.emit_slot[ne]) * H + h) * DV + grow) * DK;
+            // S_t = a S_{t-1} + beta (v - a S_{t-1} k^) k^^T = cn (R + wr k_t^T) with the raw key
+            const float wr = sb[t] * (sv[t][lrow] - a * ut) * kn / cn;
 #pragma unroll
-                for (int g = 0; g < E4; ++g)
-                    *reinterpret_cast<float4 *>(dst + (g * kLanesPerRow + sub) * 4) = S[g];
+            for (int g = 0; g < E4; ++g) {
+                R[g].x = fmaf(wr, kv[g].x, R[g].x);
+                R[g].y = fmaf(wr, kv[g].y, R[g].y);
+                R[g].z = fmaf(wr, kv[g].z, R[g].z);
+                R[g].w = fmaf(wr, kv[g].w, R[g].w);
+            }
+            c = cn;
+            if (ne < ne_end && P.emit_after[ne] == t0 + t + 1) {
+                store_scaled(P.emit_base + ((((int64_t)b * P.M + P.emit_slot[ne]) * H + h) * DV + grow) * DK, c);
                 ++ne;
             }
         }
         if (want_o) {
+            // output of the block's last token
+            const float p = quad_sum(dot_lds(sq[nt - 1]));
+            if (sub == 0) so[nt - 1][lrow] = p * c * sqn[nt - 1];
+        }
+        // fold the decay back into the state once per block
+#pragma unroll
+        for (int g = 0; g < E4; ++g) {
+            R[g].x *= c;
+            R[g].y *= c;
+            R[g].z *= c;
+            R[g].w *= c;
+        }
+        c = 1.f;
+        if (want_o) {
             __syncthreads();
             for (int idx = tid; idx < nt * DVB; idx += NT) {
-                const int t = idx / DVB, c = idx % DVB;
-                og[((row0 + t0 + t) * H + h) * DV + blk * DVB + c] = from_f32<T>(so[t][c]);
+                const int t = idx / DVB, cc = idx % DVB;
+                og[((row0 + t0 + t) * H + h) * DV + blk * DVB + cc] = from_f32<T>(so[t][cc]);
             }
         }
     }
 
-    if (P.state_dst[r]) {
-        float *dst = P.state_dst[r] + (int64_t)h * DV * DK + (int64_t)grow * DK;
-#pragma unroll
-        for (int g = 0; g < E4; ++g)
-            *reinterpret_cast<float4 *>(dst + (g * kLanesPerRow + sub) * 4) = S[g];
-    }
+    if (P.state_dst[r]) store_scaled(P.state_dst[r] + (int64_t)h * DV * DK + (int64_t)grow * DK, 1.f);
 }
 
 template <int DK, int DV, typename T>
