@@ -63,7 +63,8 @@ void recurrent_kernel(const LaunchDesc P)
     // by one wave land on different banks
     constexpr int SK = DK + ((16 - DK) & 63);
     static_assert(E % 4 == 0 && CPT >= 1, "d_k must be a multiple of 16");
-    static_assert((kTB * kPPT) % NT == 0 || NT % (kTB * kPPT) == 0, "staging lanes cover whole waves");
+    static_assert((kTB * kPPT) % NT == 0, "staging passes cover whole waves");
+    static_assert((kTB * DVB) % NT == 0, "value staging covers whole waves");
 
     __shared__ __attribute__((aligned(16))) float sk[kTB][SK];
     __shared__ __attribute__((aligned(16))) float sq[kTB][SK];
@@ -112,6 +113,7 @@ void recurrent_kernel(const LaunchDesc P)
     const int64_t row0 = P.row0[r];
     int ne = P.emit_begin[r];
     const int ne_end = P.emit_begin[r + 1];
+    int next_emit = ne < ne_end ? P.emit_after[ne] : -1;  // span position of the next emission
     const T *qg = static_cast<const T *>(P.q);
     const T *kg = static_cast<const T *>(P.k);
     const T *vg = static_cast<const T *>(P.v);
@@ -160,44 +162,80 @@ void recurrent_kernel(const LaunchDesc P)
     for (int t0 = 0; t0 < len; t0 += kTB) {
         const int nt = min(kTB, len - t0);
         __syncthreads();
-        // keys and queries: lanes 16 t .. 16 t + 15 of the staging pass convert
-        // token t (columns part, part + 16, ...) and sum its squares
-        for (int idx = tid; idx < kTB * kPPT; idx += NT) {
-            const int t = idx / kPPT, part = idx % kPPT;
+        // Staging.  Every global load of the block is issued before the first
+        // use.  Lanes of tokens past the block read its last row (always in the
+        // span) and store zeros.  Keys and queries: lanes 16 t .. 16 t + 15 of
+        // a pass take token t (columns part, part + 16, ...) and sum its squares.
+        constexpr int KPASS = kTB * kPPT / NT >= 1 ? kTB * kPPT / NT : 1;
+        constexpr int VPL = kTB * DVB / NT;  // value loads per lane (= kTB / 4)
+        float xk[KPASS][CPT], xq[KPASS][CPT], vx[VPL];
+        float xa = 0.f, xb = 0.f;
+#pragma unroll
+        for (int ps = 0; ps < KPASS; ++ps) {
+            const int idx = tid + NT * ps, t = min(idx / kPPT, nt - 1), part = idx % kPPT;
+            const int64_t base = ((row0 + t0 + t) * H + h) * DK + part;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) xk[ps][i] = to_f32(kg[base + kPPT * i]);
+        }
+        if (want_o) {
+#pragma unroll
+            for (int ps = 0; ps < KPASS; ++ps) {
+                const int idx = tid + NT * ps, t = min(idx / kPPT, nt - 1), part = idx % kPPT;
+                const int64_t base = ((row0 + t0 + t) * H + h) * DK + part;
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) xq[ps][i] = to_f32(qg[base + kPPT * i]);
+            }
+        }
+        if (!zero_v) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int idx = tid + NT * i, t = min(idx / DVB, nt - 1), cc = idx % DVB;
+                vx[i] = to_f32(vg[((row0 + t0 + t) * H + h) * DV + blk * DVB + cc]);
+            }
+        }
+        if (tid < nt) {
+            const int64_t ab = (row0 + t0 + tid) * H + h;
+            xa = to_f32(ag[ab]);
+            xb = to_f32(bg[ab]);
+        }
+#pragma unroll
+        for (int ps = 0; ps < KPASS; ++ps) {
+            const int idx = tid + NT * ps, t = idx / kPPT, part = idx % kPPT;
+            const bool live = t < nt;
             float kk = 0.f, qq = 0.f;
-            if (t < nt) {
-                const int64_t base = ((row0 + t0 + t) * H + h) * DK;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const float x = live ? xk[ps][i] : 0.f;
+                sk[t][part + kPPT * i] = x;
+                kk = fmaf(x, x, kk);
+            }
+            if (want_o) {
 #pragma unroll
                 for (int i = 0; i < CPT; ++i) {
-                    const int j = part + kPPT * i;
-                    const float x = to_f32(kg[base + j]);
-                    sk[t][j] = x;
-                    kk = fmaf(x, x, kk);
-                    if (want_o) {
-                        const float y = to_f32(qg[base + j]);
-                        sq[t][j] = y;
-                        qq = fmaf(y, y, qq);
-                    }
+                    const float y = live ? xq[ps][i] : 0.f;
+                    sq[t][part + kPPT * i] = y;
+                    qq = fmaf(y, y, qq);
                 }
             }
             kk = row16_sum(kk);
             qq = row16_sum(qq);
-            if (part == 0 && t < nt) {
+            if (part == 0 && live) {
                 skn[t] = norm_k ? inv_norm(kk) : 1.f;
                 sqn[t] = norm_q ? inv_norm(qq) : 1.f;
             }
         }
-        for (int idx = tid; idx < nt * DVB; idx += NT) {
-            const int t = idx / DVB, cc = idx % DVB;
-            sv[t][cc] = zero_v ? 0.f : to_f32(vg[((row0 + t0 + t) * H + h) * DV + blk * DVB + cc]);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int idx = tid + NT * i, t = idx / DVB;
+            sv[t][idx % DVB] = (t < nt && !zero_v) ? vx[i] : 0.f;
         }
         if (tid < nt) {
-            const int64_t ab = (row0 + t0 + tid) * H + h;
-            sa[tid] = to_f32(ag[ab]);
-            sb[tid] = to_f32(bg[ab]);
+            sa[tid] = xa;
+            sb[tid] = xb;
         }
         __syncthreads();
 
+#pragma unroll 2
         for (int t = 0; t < nt; ++t) {
             float4 kv[E4];
             load_row(sk[t], kv);
@@ -226,7 +264,8 @@ void recurrent_kernel(const LaunchDesc P)
                 cn = 1.f;
             }
             // S_t = a S_{t-1} + beta (v - a S_{t-1} k^) k^^T = cn (R + wr k_t^T) with the raw key
-            const float wr = sb[t] * (sv[t][lrow] - a * ut) * kn / cn;
+            // (1/cn to within an ulp: a relative error of 1e-7 in one token's update)
+            const float wr = sb[t] * (sv[t][lrow] - a * ut) * kn * __builtin_amdgcn_rcpf(cn);
 #pragma unroll
             for (int g = 0; g < E4; ++g) {
                 R[g].x = fmaf(wr, kv[g].x, R[g].x);
@@ -235,9 +274,10 @@ void recurrent_kernel(const LaunchDesc P)
                 R[g].w = fmaf(wr, kv[g].w, R[g].w);
             }
             c = cn;
-            if (ne < ne_end && P.emit_after[ne] == t0 + t + 1) {
+            if (next_emit == t0 + t + 1) {
                 store_scaled(P.emit_base + ((((int64_t)b * P.M + P.emit_slot[ne]) * H + h) * DV + grow) * DK, c);
                 ++ne;
+                next_emit = ne < ne_end ? P.emit_after[ne] : -1;
             }
         }
         if (want_o) {
