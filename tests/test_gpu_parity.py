@@ -544,6 +544,21 @@ def test_strong_decay_gates(gdn, kernel, alpha):
 
 
 @pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_gates_erase_the_state(gdn, kernel, dtype):
+    """alpha = 0 at every fifth row: the state before such a token is dropped
+    (S_t = beta_t v_t k^_t^T).  The per-token kernel carries the decay as a
+    running scalar and has to fold a zero in at once; the chunked kernel takes
+    log2 of the gate (clamped), so its result differs by a negligible term."""
+    for op in ("tail", "resume", "prefill"):
+        w = _small(op, dtype, 128, 128, seed=71)
+        a = w.alpha.clone()
+        a[::5] = 0
+        w.alpha = a
+        _check_workload(gdn, w, kernel, label=f"zero-gates-{op}-{dtype}")
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
 def test_zero_values_decaying_state(gdn, kernel):
     """v = 0 from a stored state: nothing is written and the state only decays.
     Over 2^-78 it keeps its relative accuracy (oracle parity); over 2^-700,
