@@ -167,6 +167,8 @@ gdn_status set_state_out(std::vector<Work> &work, float *state_out, const gdn_sh
     return GDN_OK;
 }
 
+bool misaligned(const void *p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
 // Validate pointers, pick the kernel and queue the launches.
 gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
                const void *alpha, const void *beta, void *o,
@@ -179,7 +181,23 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
             return fail(GDN_ERR_INVALID_ARGUMENT, "k, v, alpha and beta must be non-NULL");
         if (o && !q) return fail(GDN_ERR_INVALID_ARGUMENT, "o is set but q is NULL");
     }
-    const int32_t kern = kernel_choice(s);
+    // inputs at their element size; states are read and written as float4
+    const uintptr_t esz = s->dtype == GDN_DTYPE_F32 ? 4 : 2;
+    if (misaligned(q, esz) || misaligned(k, esz) || misaligned(v, esz) || misaligned(alpha, esz) ||
+        misaligned(beta, esz) || misaligned(o, esz))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, alpha, beta and o must be aligned to their element size");
+    if (misaligned(init_base, 16) || misaligned(emit_base, 16))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "the checkpoint store must be 16-byte aligned");
+    for (const Work &w : work)
+        if (misaligned(w.dst, 16)) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out must be 16-byte aligned");
+    // the chunked kernel copies 16-byte pieces of q, k, v rows and stores whole o rows
+    const bool rows16 = !misaligned(q, 16) && !misaligned(k, 16) && !misaligned(v, 16) && !misaligned(o, 16);
+    int32_t kern = kernel_choice(s);
+    if (kern == 1 && !rows16) {
+        if (s->flags & GDN_KERNEL_CHUNKED)
+            return fail(GDN_ERR_UNSUPPORTED, "GDN_KERNEL_CHUNKED: q, k, v and o must be 16-byte aligned");
+        kern = 0;
+    }
     if (kern < 0)
         return fail(GDN_ERR_UNSUPPORTED,
                     "GDN_KERNEL_CHUNKED: no chunked kernel for d_k = %d, d_v = %d, dtype %d, flags 0x%x "
@@ -505,6 +523,7 @@ GDN_API gdn_status gdn_prefill_emit_checkpoints_split(const gdn_shape *shape, co
     if (!workspace || workspace_bytes < need)
         return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
+    if (misaligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     const int64_t slot = (int64_t)shape->H * shape->dv * shape->dk;
     if (ranges_overlap(workspace, need, state_out, (size_t)shape->B * slot * sizeof(float)) ||
         (M > 0 && ranges_overlap(workspace, need, ckpt_states, (size_t)shape->B * M * slot * sizeof(float))))

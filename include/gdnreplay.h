@@ -31,7 +31,12 @@
  * Conventions for all entry points:
  *  - Device pointers (q, k, v, alpha, beta, o, state_out, ckpt_states) must
  *    be device memory of the current HIP device; arguments prefixed h_ are
- *    host arrays, read during the call only.  The caller owns every buffer.
+ *    host arrays, read during the call only.  q, k, v, alpha, beta and o must
+ *    be aligned to their element size and the float32 state buffers to 16
+ *    bytes (GDN_ERR_INVALID_ARGUMENT otherwise).  The chunked kernel also
+ *    needs 16-byte aligned q, k, v and o; a call whose rows are not runs on
+ *    the per-token kernel instead (GDN_ERR_UNSUPPORTED under
+ *    GDN_KERNEL_CHUNKED).  The caller owns every buffer.
  *    The library allocates nothing, keeps no device state beyond its code
  *    object and never synchronises: work is queued on `stream` (NULL = the
  *    null stream) and results are ready when that stream has drained.
@@ -92,9 +97,10 @@ const char *gdn_version(void);
 const char *gdn_last_error(void);
 
 /*
- * Which kernel the entry points would run for this shape: 0 = the per-token
- * float32 kernel, 1 = the chunked matrix-core kernel, -1 = the shape (or a
- * GDN_KERNEL_* request in its flags) is not supported.  Host only.
+ * Which kernel the entry points would run for this shape (with 16-byte
+ * aligned q, k, v and o): 0 = the per-token float32 kernel, 1 = the chunked
+ * matrix-core kernel, -1 = the shape (or a GDN_KERNEL_* request in its flags)
+ * is not supported.  Host only.
  */
 int32_t gdn_kernel_for(const gdn_shape *shape);
 

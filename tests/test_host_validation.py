@@ -79,6 +79,33 @@ def test_tail_span_outside_stored_tail_rows(gdn):
     assert st == 1 and "not stored" in msg
 
 
+def test_pointer_alignment(gdn):
+    """Inputs must sit at their element size, states at 16 bytes; a chunked
+    launch that is required needs 16-byte aligned rows.  All rejected before
+    any launch."""
+    lib = gdn.load()
+
+    def call(q=FAKE, k=FAKE, alpha=FAKE, state=FAKE, flags=1):
+        sh = gdn._Shape(B=2, H=2, dk=128, dv=128, dtype=1, flags=flags)
+        off, m = gdn._i64([0, 10, 20]), gdn._i64([10, 10])
+        p = ctypes.c_void_p(FAKE)
+        st = lib.gdn_tail_replay(ctypes.byref(sh), ctypes.c_void_p(q), ctypes.c_void_p(k), p,
+                                 ctypes.c_void_p(alpha), p, gdn._p64(off), None, gdn._p64(m), 5, 100,
+                                 ctypes.c_void_p(state), p, None, None)
+        return st, lib.gdn_last_error().decode()
+
+    st, msg = call(q=FAKE + 1)
+    assert st == 1 and "element size" in msg
+    st, msg = call(alpha=FAKE + 3)
+    assert st == 1 and "element size" in msg
+    st, msg = call(state=FAKE + 8)
+    assert st == 1 and "16-byte" in msg
+    # bf16 rows two bytes off: fine for the per-token kernel, refused when the
+    # chunked kernel is required
+    st, msg = call(k=FAKE + 2, flags=1 | 512)
+    assert st == 2 and "16-byte" in msg
+
+
 def test_chunked_required_but_unavailable_for_f32(gdn):
     st, msg = _call_tail(gdn, {"dtype": 0, "flags": 512})
     assert st == 2 and "CHUNKED" in msg
@@ -150,6 +177,7 @@ def test_split_prefill_workspace_checks(gdn):
 
     assert call(None, need) == 1
     assert call(0x900000000, need - 1) == 1
+    assert call(0x900000008, need) == 1 and b"16-byte" in lib.gdn_last_error()
     # the workspace may not overlap the final states
     assert call(0x900000000, need, state=0x900000000 + 4096) == 1
     assert b"overlaps" in lib.gdn_last_error()
