@@ -543,6 +543,37 @@ def test_strong_decay_gates(gdn, kernel, alpha):
         _check_workload(gdn, w, kernel, label=f"decay-{op}-{alpha[0]}")
 
 
+def _shifted(t, elems=1):
+    """A contiguous copy of t that starts `elems` elements past an aligned allocation."""
+    buf = torch.empty(t.numel() + 16, dtype=t.dtype, device=t.device)
+    v = buf[elems:elems + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("op", ["tail", "resume", "prefill"])
+def test_rows_off_16_bytes_run_on_the_per_token_kernel(gdn, op):
+    """bf16 q, k, v two bytes past a 16-byte boundary: the chunked kernel copies
+    rows in 16-byte pieces, so the library runs the per-token kernel, whose
+    results match the oracle; requiring the chunked kernel is refused."""
+    w = _small(op, "bf16", 128, 128, seed=81)
+    W.poison_outside(w, PT.spans_of(w))
+    PT.to_device(w)
+    w.q, w.k, w.v = _shifted(w.q), _shifted(w.k), _shifted(w.v)
+    assert w.k.data_ptr() % 16 == 2
+    _log(f"[rows-off-16] {w.name} op={op}")
+    res = PT.run_library(gdn, w)
+    torch.cuda.synchronize()
+    ref = PT.oracle_pairs(w, _all_pairs(w), init=PT.init_for(w), emit=PT.emit_for(w))
+    worst = PT.compare(w, ref, res["state"], res["o"], res.get("ckpt"), label="rows-off-16")
+    _log(f"[rows-off-16] worst rel err {worst}")
+    # the per-token kernel's float32 accuracy, not the chunked kernel's
+    assert worst["state"] < 1e-5
+    with pytest.raises(gdn.GDNError) as e:
+        PT.run_library(gdn, w, flags_extra=gdn.KERNEL_CHUNKED)
+    assert e.value.status == 2
+
+
 @pytest.mark.parametrize("kernel", ["recurrent", "auto"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_zero_gates_erase_the_state(gdn, kernel, dtype):
