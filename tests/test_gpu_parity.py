@@ -103,6 +103,51 @@ def test_small_parity(gdn, op, dtype, dk, dv, kernel):
     _check_workload(gdn, w, kernel, label=f"small-{op}")
 
 
+def _random_case(rng, i):
+    """One seeded random small case: operation, widths, dtype, normalisation
+    flags, lengths (including lengths just around the per-token kernel's
+    16-token blocks and the chunked kernel's 32-token chunks) and checkpoint
+    positions."""
+    op = ["tail", "resume", "prefill"][i % 3]
+    dk, dv = [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128)][int(rng.integers(6))]
+    if i % 4 == 0:
+        dk = dv = 128  # keep the chunked kernel in the mix
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.choice([1, 15, 16, 17, 31, 32, 33, 47, 64, 65, 130, 257], size=B)]
+    seed = 1000 + i
+    if op == "tail":
+        w = W.tail(seed=seed, B=B, H=H, d=dk, m_list=[max(n, 1) * 4 for n in lens], r_num=25, r_den=100,
+                   dtype=dtype, pad=3)
+    elif op == "resume":
+        N = max(lens) + 40
+        w = W.resume(seed=seed, B=B, H=H, d=dk, N=N, M=3, dtype=dtype,
+                     depths=[int(rng.integers(0, N + 1)) for _ in range(B)])
+    else:
+        # the same number of checkpoints for every request, at most its length
+        w = W.prefill(seed=seed, B=B, H=H, d=dk, N=max(lens), M=min(3, min(lens)), dtype=dtype, lengths=lens)
+    if dv != dk:
+        g = torch.Generator().manual_seed(seed + 100)
+        w.v = torch.randn(w.rows, w.H, dv, generator=g).to(w.v.dtype)
+        w.dv = dv
+        if w.ckpt_states is not None:
+            w.ckpt_states = 0.05 * torch.randn(w.B, w.ckpt_states.shape[1], w.H, dv, dk, generator=g)
+    flags = [W.NORMALIZE_K | W.NORMALIZE_Q, W.NORMALIZE_K, W.NORMALIZE_K | W.NORMALIZE_Q][i % 3]
+    w.flags = flags
+    return w
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+def test_random_small_cases(gdn, kernel):
+    """A seeded sweep of 24 random small cases (operations, widths, dtypes,
+    flags, ragged lengths around block and chunk edges, emissions) against the
+    oracle on every pair."""
+    rng = np.random.default_rng(2024)
+    for i in range(24):
+        w = _random_case(rng, i)
+        _check_workload(gdn, w, kernel, label=f"random-{i}")
+
+
 # --- the headline workloads at full size, sampled pairs ------------------------
 
 def _sample_pairs(w, n, seed):
