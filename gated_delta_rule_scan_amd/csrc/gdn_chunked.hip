@@ -1185,6 +1185,17 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 {
     __shared__ Smem sm;
     const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
+    // work items without outputs (the split prefill's zero-start replays and
+    // transition products) take the path that skips the query side entirely
+    if (WANT_O && (P.wflags[xcd_remap(blockIdx.x, gridDim.x) / P.H] & kWorkNoOut)) {
+        switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+            case 0: wave_main<0, false, NORM_Q, ALIAS>(P, sm, sm_lds); break;
+            case 1: wave_main<1, false, NORM_Q, ALIAS>(P, sm, sm_lds); break;
+            case 2: wave_main<2, false, NORM_Q, ALIAS>(P, sm, sm_lds); break;
+            default: wave_main<3, false, NORM_Q, ALIAS>(P, sm, sm_lds); break;
+        }
+        return;
+    }
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
         case 0: wave_main<0, WANT_O, NORM_Q, ALIAS>(P, sm, sm_lds); break;
         case 1: wave_main<1, WANT_O, NORM_Q, ALIAS>(P, sm, sm_lds); break;
