@@ -56,7 +56,8 @@
 // the state chain (converted to the fp16 tiles one chunk ahead), V rows one
 // chunk ahead; wave 3 issues the key and V copies of the whole workgroup.
 // Outputs of a chunk are staged in LDS and stored as whole rows during the
-// next one.
+// next one.  Work items without outputs (zero-start replays and transition
+// products of the split prefill) run the instantiation without the query side.
 //
 // Per chunk n, two barriers: after the first, the state chain of n up to B~
 // (which needs no T), the conversion of n + 1 and the last step of T for n;
