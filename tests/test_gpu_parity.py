@@ -749,3 +749,60 @@ def test_unnormalised_queries(gdn, kernel, op):
     w.q = (w.q.float() * scale).to(w.q.dtype)
     w.flags = W.NORMALIZE_K
     _check_workload(gdn, w, kernel, label=f"rawq-{op}")
+
+
+# --- capture in a HIP graph -------------------------------------------------------
+
+def test_replays_captured_in_a_graph(gdn):
+    """The entry points only validate on the host and queue kernels on the
+    caller's stream, so a serving loop can capture them in a HIP graph: a
+    captured chunked tail replay, split prefill and float32 per-token resume,
+    replayed three times with eager work in between, reproduce the eager
+    results bit for bit each time."""
+    wt = W.tail(seed=91, B=2, H=4, m_list=[900, 640], r_num=10, r_den=100, pad=2)
+    wr = W.resume(seed=92, B=2, H=2, d=64, N=300, M=3, dtype="f32", depths=[290, 150])
+    wp = W.prefill(seed=93, B=1, H=2, d=128, N=1000, M=3, lengths=[1000])
+    for w in (wt, wr, wp):
+        PT.to_device(w)
+    st_t = torch.empty(wt.B, wt.H, 128, 128, device="cuda")
+    o_t = torch.empty_like(wt.v)
+    st_r = torch.empty(wr.B, wr.H, 64, 64, device="cuda")
+    o_r = torch.empty_like(wr.v)
+    cs_p = torch.empty(1, 3, 2, 128, 128, device="cuda")
+    st_p = torch.empty(1, 2, 128, 128, device="cuda")
+    o_p = torch.empty_like(wp.v)
+    ws = torch.empty(gdn.prefill_split_workspace_bytes(1, 2, 128, 128), dtype=torch.uint8, device="cuda")
+
+    def work():
+        gdn.tail_replay(wt.q, wt.k, wt.v, wt.alpha, wt.beta, wt.tok_offset, wt.m, wt.r_num, wt.r_den,
+                        first_pos=wt.first_pos, flags=wt.flags, state_out=st_t, o=o_t)
+        gdn.resume(wr.q, wr.k, wr.v, wr.alpha, wr.beta, wr.tok_offset, wr.ckpt_pos, wr.ckpt_states,
+                   wr.depth, first_pos=wr.first_pos, flags=wr.flags, state_out=st_r, o=o_r)
+        gdn.prefill_emit_checkpoints_split(wp.q, wp.k, wp.v, wp.alpha, wp.beta, wp.tok_offset,
+                                           wp.ckpt_pos, flags=wp.flags, ckpt_states=cs_p,
+                                           state_out=st_p, o=o_p, workspace=ws)
+
+    outs = (st_t, o_t, st_r, o_r, cs_p, st_p, o_p)
+    for t in outs:
+        t.zero_()  # o is written on span rows only; the other rows stay zero
+    work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()  # eager work between replays; the replay rewrites every result
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _log(f"[graph] replay {rep}")
+        for i, (t, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(t, e), f"replay {rep}: output {i} differs from the eager run"
