@@ -51,7 +51,9 @@
 // float32.
 //
 // Work split: one workgroup of 4 waves per (request, head), two workgroups per
-// CU (LDS 80 KB each).  Inputs go from HBM straight into LDS with
+// CU (LDS 80 KB each).  Launches with at most one workgroup per CU use eight
+// waves instead: waves 0-3 the state side, waves 4-7 the key side of the same
+// schedule, so that the two overlap within each phase.  Inputs go from HBM straight into LDS with
 // global_load_lds_dwordx4: raw bf16 key and query rows two chunks ahead of
 // the state chain (converted to the fp16 tiles one chunk ahead), V rows one
 // chunk ahead; wave 3 issues the key and V copies of the whole workgroup.
@@ -784,9 +786,14 @@ __device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, gchar *ob
 // One wave's part of a (request, head).  ROLE is the wave index: it selects
 // the wave's value rows and key-side task, and as a compile-time constant it
 // removes the per-chunk role branches.
-template <int ROLE, bool WANT_O, bool NORM_Q, bool ALIAS>
+template <int ROLE, bool WANT_O, bool NORM_Q, bool ALIAS, bool SPLIT = false>
 __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_t sm_lds)
 {
+    // SPLIT (eight waves): waves 0-3 carry the state chain and waves 4-7 the
+    // key side of the same schedule, each under role ROLE % 4; without SPLIT
+    // every wave does both.  Both groups pass the same barriers.
+    constexpr bool STATE = !SPLIT || ROLE < 4;
+    constexpr bool KEY = !SPLIT || ROLE >= 4;
 
     const int Lg = xcd_remap(blockIdx.x, gridDim.x);
     const int h = Lg % P.H;
@@ -794,7 +801,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     const int b = P.req[r];
     const int H = P.H;
     const int tid = threadIdx.x;
-    constexpr int w = ROLE;
+    constexpr int w = ROLE & 3;
     const Lane L = make_lane(tid, w, H);
     const int lane = L.lane, l32 = L.l32, hi32 = L.hi32;
     const int dv = 32 * w + l32;
@@ -820,7 +827,11 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     // ---- state S^T = 2^{-sigma} Sacc: tile a covers d_k rows 32a..32a+31; the
     // lane holds value row dv and d_k rows 8(j/4) + 4*hi32 + j%4 of each tile.
     floatx16 Sacc[4];
-    if (wf & kWorkIdentity) {
+    float sigma = 0.f;  // S = 2^{-sigma} Sacc
+    float mb = 0.f;     // bound on max |Sacc| per value column (lanes l, l ^ 32)
+    if (!STATE) {
+        // the key-side waves hold no state
+    } else if (wf & kWorkIdentity) {
         // lane holds d_k rows 32 a + 8 (j/4) + 4 hi32 + j%4 of value row dv
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -845,9 +856,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
 #pragma unroll
             for (int j = 0; j < 16; ++j) Sacc[a][j] = 0.f;
     }
-    float sigma = 0.f;  // S = 2^{-sigma} Sacc
-    float mb = 0.f;     // bound on max |Sacc| per value column (lanes l, l ^ 32)
-    if (len > 0) {
+    if (STATE && len > 0) {
         float mx = 0.f;
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -865,7 +874,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         }
     }
 
-    if (zero_v) {
+    if (STATE && zero_v) {
         // both V buffers of this wave's columns stay zero (no copies, no output staging)
         typedef uint32_t u32x4z __attribute__((ext_vector_type(4)));
         const u32x4z zz = {0u, 0u, 0u, 0u};
@@ -893,7 +902,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     // (chunk index % 2), and serve as keys, queries and values until the
     // copy of the chunk two ahead replaces them.
     constexpr uint32_t RAW1 = OFF_KQR + C * DK * 2;  // second raw tile
-    if (cur.lc > 0) {
+    if (KEY && cur.lc > 0) {
         if (!zero_v && !ALIAS) dma_v(sm_lds, 0, G, cur.t0, cur.lc, w, L);
         load_kq<0>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
         load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
@@ -901,14 +910,16 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     }
     lds_barrier();
     if (cur.lc > 0) {
-        if (ALIAS) key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L, OFF_KQR, OFF_KQR);
-        else key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
+        if (KEY) {
+            if (ALIAS) key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L, OFF_KQR, OFF_KQR);
+            else key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
+        }
         lds_barrier();  // the raw tiles are free again (ALIAS: tile 0 keeps chunk 0's values)
-        if (nx.lc > 0) {
+        if (KEY && nx.lc > 0) {
             load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L, ALIAS ? RAW1 : OFF_KQR);
             load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
         }
-        key_side_tasks<WANT_O>(sm, 0, w, L);
+        if (KEY) key_side_tasks<WANT_O>(sm, 0, w, L);
     }
 
     int p = 0;   // key-side buffer of the current chunk
@@ -923,7 +934,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();  // key-side tasks of `cur` complete; previous state step done
         if (WANT_O && lc_pend > 0) {
-            store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
+            if (STATE) store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
             lc_pend = 0;
         }
         // ---- state side of `cur` ------------------------------------------------
@@ -933,7 +944,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         float *cwl = sm.cw[w][0];
 
         // key side of `nx`: conversion (independent of the state chain above)
-        if (nx.lc > 0) {
+        if (KEY && nx.lc > 0) {
             if (ALIAS) {
                 const uint32_t rawn = kp ? OFF_KQR : RAW1;  // raw tile of `nx`
                 key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L, rawn, rawn);
@@ -941,6 +952,9 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
                 key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
             }
         }
+        floatx16 Y = {}, Z = {};
+        int eB = 0;
+        if (STATE) {
         // Y = K^ Sacc^T and Z = Q^ Sacc^T (Sacc within the fp16 band by construction)
         // (all fragments are read first, so that the reads overlap)
         half8 kf[8], qf[8];
@@ -949,7 +963,6 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             kf[m] = lds_ld<half8>(sm, kbuf + L.yz + 32 * m);
             if (WANT_O) qf[m] = lds_ld<half8>(sm, kbuf + 2 * KBUF + L.yz + 32 * m);
         }
-        floatx16 Y = {}, Z = {};
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const half8 sf = to_frag(Sacc[m >> 1], m & 1);
@@ -1002,10 +1015,10 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
                 }
             }
         }
-        int eB = 0;
         if (out_of_band(bm)) eB = f16_adjust(wave_max(bm));
         if (eB != 0) Y *= ldexpf(1.f, eB);
-        if (w == 3) {
+        }  // STATE
+        if (KEY && w == 3) {
             // the last T step is on the critical path of this phase: it takes
             // issue priority over the co-resident workgroup's waves
             __builtin_amdgcn_s_setprio(2);
@@ -1013,6 +1026,26 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             __builtin_amdgcn_s_setprio(0);
         }
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
+        // raw keys of `nx2` before the task, queries (and gates) after it; all
+        // before the output stores (see the wait above)
+        const bool has2 = nx2.lc > 0;
+        const int kt2 = has2 ? nx2.t0 : cur.t0;
+        const int klc2 = has2 ? nx2.lc : cur.lc;
+        auto key_phase = [&]() {
+            if (w == 3) load_k_all(sm_lds, G, kt2, klc2, L, ALIAS ? (kp ? RAW1 : OFF_KQR) : OFF_KQR);
+            // V of `nx` into the other V buffer (its staged outputs went out after the
+            // first barrier; without a next chunk, rows of `cur` are copied and ignored)
+            if (!zero_v && !ALIAS && w == 3) {
+                const bool has1 = nx.lc > 0;
+                dma_v_all(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L);
+            }
+            if (w != 3) __builtin_amdgcn_s_setprio(1);  // the longer tasks of this phase go first
+            if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
+            if (w != 3) __builtin_amdgcn_s_setprio(0);
+            load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
+        };
+        if (SPLIT && KEY) key_phase();
+        if (STATE) {
         // operands of `cur` that are complete now are read before the tasks
         const half8 tfr0 = tr_frag_st(sm, OFF_TT, 0, L);
         const half8 tfr1 = tr_frag_st(sm, OFF_TT, 1, L);
@@ -1023,22 +1056,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         }
         const float tsc = sm.tsc;
         const float gCp = sm.gC[p];
-        // raw keys of `nx2` before the task, queries (and gates) after it; all
-        // before the output stores (see the wait above)
-        const bool has2 = nx2.lc > 0;
-        const int kt2 = has2 ? nx2.t0 : cur.t0;
-        const int klc2 = has2 ? nx2.lc : cur.lc;
-        if (w == 3) load_k_all(sm_lds, G, kt2, klc2, L, ALIAS ? (kp ? RAW1 : OFF_KQR) : OFF_KQR);
-        // V of `nx` into the other V buffer (its staged outputs went out after the
-        // first barrier; without a next chunk, rows of `cur` are copied and ignored)
-        if (!zero_v && !ALIAS && w == 3) {
-            const bool has1 = nx.lc > 0;
-            dma_v_all(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L);
-        }
-        if (w != 3) __builtin_amdgcn_s_setprio(1);  // the longer tasks of this phase go first
-        if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
-        if (w != 3) __builtin_amdgcn_s_setprio(0);
-        load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
+        if (!SPLIT) key_phase();
 
         // U = (T diag(beta)) B~
         floatx16 U = {};
@@ -1167,6 +1185,8 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         if (cur.ne < ne_end && P.emit_after[cur.ne] == cur.t0 + lc)
             store_state(P.emit_base + (((int64_t)b * P.M + P.emit_slot[cur.ne]) * H + h) * DV * DK, Sacc, sigma,
                         w, l32, hi32);
+        }  // STATE
+        if (SPLIT && !STATE && out) lc_pend = lc;  // the key-side waves pass the same final barrier
         cur = nx;
         nx = nx2;
         p ^= 1;
@@ -1176,9 +1196,9 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
 
     if (WANT_O && lc_pend > 0) {
         lds_barrier();  // the last staged outputs are complete
-        store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
+        if (STATE) store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
     }
-    if (P.state_dst[r]) store_state(P.state_dst[r] + (int64_t)h * DV * DK, Sacc, sigma, w, l32, hi32);
+    if (STATE && P.state_dst[r]) store_state(P.state_dst[r] + (int64_t)h * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
 template <bool WANT_O, bool NORM_Q, bool ALIAS>
@@ -1205,6 +1225,48 @@ __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
     }
 }
 
+// Eight waves per workgroup for launches with at most one workgroup per CU:
+// waves 0-3 carry the state chain, waves 4-7 the key side (same schedule and
+// LDS layout as chunked_kernel), so that the two halves of each phase overlap.
+template <bool WANT_O, bool NORM_Q, bool ALIAS>
+__global__ __launch_bounds__(2 * NT, 2) void chunked8_kernel(const LaunchDesc P)
+{
+    __shared__ Smem sm;
+    const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // (work items without outputs run this path with their stores off; only
+    // the four-wave kernel has the path without the query side, for the large
+    // launches where the split prefill's side scans matter)
+    switch (wv) {
+        case 0: wave_main<0, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+        case 1: wave_main<1, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+        case 2: wave_main<2, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+        case 3: wave_main<3, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+        case 4: wave_main<4, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+        case 5: wave_main<5, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+        case 6: wave_main<6, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+        default: wave_main<7, WANT_O, NORM_Q, ALIAS, true>(P, sm, sm_lds); break;
+    }
+}
+
+int cu_count() {
+    static const int n = [] {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        return c;
+    }();
+    return n;
+}
+
+template <bool WANT_O, bool NORM_Q, bool ALIAS>
+void launch_variant(const LaunchDesc &d, int nwg, hipStream_t s) {
+    if (nwg <= cu_count())
+        hipLaunchKernelGGL((chunked8_kernel<WANT_O, NORM_Q, ALIAS>), dim3(nwg), dim3(2 * NT), 0, s, d);
+    else
+        hipLaunchKernelGGL((chunked_kernel<WANT_O, NORM_Q, ALIAS>), dim3(nwg), dim3(NT), 0, s, d);
+}
+
 }  // namespace
 
 bool chunked_supported(int dk, int dv, Elem e) {
@@ -1216,17 +1278,18 @@ hipError_t launch_chunked(const LaunchDesc &d, int dk, int dv, Elem e, hipStream
     const int nwg = d.nreq * d.H;
     if (nwg == 0) return hipSuccess;
     const bool want_o = d.o != nullptr, norm_q = (d.flags & kNormQ) != 0, alias = (d.flags & kAliasQKV) != 0;
-    const dim3 grid(nwg), block(NT);
+    // one workgroup per CU or fewer: the eight-wave kernel; otherwise two
+    // four-wave workgroups share a CU
     if (alias) {
-        if (want_o && norm_q) hipLaunchKernelGGL((chunked_kernel<true, true, true>), grid, block, 0, s, d);
-        else if (want_o) hipLaunchKernelGGL((chunked_kernel<true, false, true>), grid, block, 0, s, d);
-        else if (norm_q) hipLaunchKernelGGL((chunked_kernel<false, true, true>), grid, block, 0, s, d);
-        else hipLaunchKernelGGL((chunked_kernel<false, false, true>), grid, block, 0, s, d);
+        if (want_o && norm_q) launch_variant<true, true, true>(d, nwg, s);
+        else if (want_o) launch_variant<true, false, true>(d, nwg, s);
+        else if (norm_q) launch_variant<false, true, true>(d, nwg, s);
+        else launch_variant<false, false, true>(d, nwg, s);
     } else {
-        if (want_o && norm_q) hipLaunchKernelGGL((chunked_kernel<true, true, false>), grid, block, 0, s, d);
-        else if (want_o) hipLaunchKernelGGL((chunked_kernel<true, false, false>), grid, block, 0, s, d);
-        else if (norm_q) hipLaunchKernelGGL((chunked_kernel<false, true, false>), grid, block, 0, s, d);
-        else hipLaunchKernelGGL((chunked_kernel<false, false, false>), grid, block, 0, s, d);
+        if (want_o && norm_q) launch_variant<true, true, false>(d, nwg, s);
+        else if (want_o) launch_variant<true, false, false>(d, nwg, s);
+        else if (norm_q) launch_variant<false, true, false>(d, nwg, s);
+        else launch_variant<false, false, false>(d, nwg, s);
     }
     return hipGetLastError();
 }
