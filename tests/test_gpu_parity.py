@@ -806,3 +806,51 @@ def test_replays_captured_in_a_graph(gdn):
         _log(f"[graph] replay {rep}")
         for i, (t, e) in enumerate(zip(outs, eager)):
             assert torch.equal(t, e), f"replay {rep}: output {i} differs from the eager run"
+
+
+# --- four-wave and eight-wave launches ----------------------------------------------
+
+def _heads(w, n):
+    """The same workload restricted to heads 0 .. n-1."""
+    import dataclasses
+    sub = dataclasses.replace(w, H=n, q=w.q[:, :n].contiguous(), k=w.k[:, :n].contiguous(),
+                              v=w.v[:, :n].contiguous(), alpha=w.alpha[:, :n].contiguous(),
+                              beta=w.beta[:, :n].contiguous())
+    if w.ckpt_states is not None:
+        sub.ckpt_states = w.ckpt_states[:, :, :n].contiguous()
+    return sub
+
+
+@pytest.mark.parametrize("op", ["tail", "resume", "prefill"])
+def test_four_and_eight_wave_launches_agree(gdn, op):
+    """A launch with more workgroups than CUs runs the chunked kernel with four
+    waves per workgroup, a smaller one with eight (state and key side on
+    separate waves).  With 300 workgroups the four-wave kernel meets the oracle
+    on sampled pairs (emissions at chunk edges, ragged and empty spans), and
+    heads 0-7 run alone (eight waves) give the same results bit for bit."""
+    if op == "tail":
+        w = W.tail(seed=95, B=3, H=100, d=128, m_list=[700, 1, 333], r_num=10, r_den=100, pad=7)
+    elif op == "resume":
+        w = W.resume(seed=96, B=3, H=100, d=128, N=300, M=5, depths=[0, 151, 299])
+    else:
+        w = W.prefill(seed=97, B=2, H=150, d=128, N=260, M=6, lengths=[260, 97],
+                      positions=[[1, 31, 32, 33, 200, 260], [5, 64, 65, 66, 96, 97]])
+    big = w
+    W.poison_outside(big, PT.spans_of(big))
+    PT.to_device(big)
+    _log(f"[waves] {big.name} op={op} workgroups={big.B * big.H}")
+    res = PT.run_library(gdn, big)
+    torch.cuda.synchronize()
+    pairs = _sample_pairs(big, 10, 98) + [(0, 5), (big.B - 1, 3)]
+    ref = PT.oracle_pairs(big, pairs, init=PT.init_for(big), emit=PT.emit_for(big))
+    PT.compare(big, ref, res["state"], res["o"], res.get("ckpt"), label=f"waves-{op}")
+    small = _heads(big, 8)
+    res8 = PT.run_library(gdn, small)
+    torch.cuda.synchronize()
+    assert torch.equal(res8["state"], res["state"][:, :8])
+    spans = PT.spans_of(big)
+    for b, (p0, n) in enumerate(spans):
+        r0 = big.tok_offset[b] + (p0 - big.first_pos[b])
+        assert torch.equal(res8["o"][r0:r0 + n], res["o"][r0:r0 + n, :8])
+    if res.get("ckpt") is not None:
+        assert torch.equal(res8["ckpt"], res["ckpt"][:, :, :8])
