@@ -563,6 +563,24 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
     }
 }
 
+// Raw key (and query) rows of the 4-token blocks that wave W converts (the
+// owner map of key_side_convert), for the chunk at span token t0 with lc rows;
+// rows past the chunk are clamped to its last row.  A wave that copies exactly
+// the rows it converts may issue the copies right after its own conversion.
+template <bool WANT_Q, int W>
+__device__ __forceinline__ void load_owned(uint32_t sm_lds, const Bases &G, int t0, int lc, const Lane &L) {
+    const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.ldc;
+    constexpr int NG = WANT_Q ? 16 : 8;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        if (cvt_owner<WANT_Q>(gi) != W) continue;
+        const int kind = WANT_Q ? (gi & 1) : 0;
+        const int rb = WANT_Q ? (gi >> 1) : gi;
+        dma16(at_tok(kind ? G.q : G.k, t0, G.ts), min((uint32_t)(4 * rb + L.g) * G.ts + L.ldc, lim),
+              sm_lds + OFF_KQR + (uint32_t)(kind * C * DK * 2 + rb * 4 * DK * 2));
+    }
+}
+
 // ---- key side, part 2: T = (I + A)^{-1} in three tile tasks and a combine ----
 // Tile-task operand fragments: rows 16 b + lane%16, k-step ks covering the
 // 16-byte units 4 (lane/16) + ks (the same units on both MFMA operands).
@@ -929,6 +947,14 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     int lc_pend = 0, vb_pend = 0;
     while (cur.lc > 0) {
         const Chunk nx2 = next_chunk(P, nx, len, ne_end);
+        // raw keys of `nx2` before the task, queries (and gates) after it; all
+        // before the output stores (see the wait below)
+        const bool has2 = nx2.lc > 0;
+        const int kt2 = has2 ? nx2.t0 : cur.t0;
+        const int klc2 = has2 ? nx2.lc : cur.lc;
+        // eight waves, separate tensors: each key-side wave copies the rows it
+        // converts, as soon as its own conversion has read them
+        constexpr bool EARLY = SPLIT && !ALIAS;
         // every load this wave issued has landed; the barrier then publishes the
         // raw key/query rows and the staged outputs to all waves
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -951,6 +977,10 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             } else {
                 key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
             }
+        }
+        if (EARLY && KEY) {
+            load_owned<WANT_O, w>(sm_lds, G, kt2, klc2, L);
+            load_kq<1, false>(pf, sm_lds, G, kt2, klc2, w, L);  // gates of `nx2`
         }
         floatx16 Y = {}, Z = {};
         int eB = 0;
@@ -1026,13 +1056,8 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             __builtin_amdgcn_s_setprio(0);
         }
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
-        // raw keys of `nx2` before the task, queries (and gates) after it; all
-        // before the output stores (see the wait above)
-        const bool has2 = nx2.lc > 0;
-        const int kt2 = has2 ? nx2.t0 : cur.t0;
-        const int klc2 = has2 ? nx2.lc : cur.lc;
         auto key_phase = [&]() {
-            if (w == 3) load_k_all(sm_lds, G, kt2, klc2, L, ALIAS ? (kp ? RAW1 : OFF_KQR) : OFF_KQR);
+            if (!EARLY && w == 3) load_k_all(sm_lds, G, kt2, klc2, L, ALIAS ? (kp ? RAW1 : OFF_KQR) : OFF_KQR);
             // V of `nx` into the other V buffer (its staged outputs went out after the
             // first barrier; without a next chunk, rows of `cur` are copied and ignored)
             if (!zero_v && !ALIAS && w == 3) {
@@ -1042,7 +1067,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             if (w != 3) __builtin_amdgcn_s_setprio(1);  // the longer tasks of this phase go first
             if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
             if (w != 3) __builtin_amdgcn_s_setprio(0);
-            load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
+            if (!EARLY) load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
         };
         if (SPLIT && KEY) key_phase();
         if (STATE) {
