@@ -854,3 +854,22 @@ def test_four_and_eight_wave_launches_agree(gdn, op):
         assert torch.equal(res8["o"][r0:r0 + n], res["o"][r0:r0 + n, :8])
     if res.get("ckpt") is not None:
         assert torch.equal(res8["ckpt"], res["ckpt"][:, :, :8])
+
+
+@pytest.mark.parametrize("B", [2, 10])
+@pytest.mark.parametrize("flags", [3, 1])
+def test_runs_are_deterministic(gdn, B, flags):
+    """The same call three times gives the same bits (64 workgroups: the
+    eight-wave chunked kernel; 320: the four-wave one; queries normalised or
+    used as stored).  No reduction or hand-off depends on timing."""
+    w = W.tail(seed=99, B=B, m=3000, r_num=10, r_den=100)
+    PT.to_device(w)
+    outs = []
+    for _ in range(3):
+        S, O, _ = gdn.tail_replay(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m, w.r_num, w.r_den,
+                                  first_pos=w.first_pos, flags=flags)
+        torch.cuda.synchronize()
+        outs.append((S.clone(), O.clone()))
+    for S, O in outs[1:]:
+        assert torch.equal(S.view(torch.int32), outs[0][0].view(torch.int32))
+        assert torch.equal(O.view(torch.int16), outs[0][1].view(torch.int16))
