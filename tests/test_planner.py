@@ -2,8 +2,9 @@
 the oracle.  CPU only (the planner does no device work).
 
 Source: "Sparse prefix caching for hybrid and recurrent LLM serving" (arXiv
-2605.05219), §3 (objective R), §4 (Theorem 1, Theorem 2, Lemma 1) and §5
-(the uniform-spacing baseline: gaps that differ by at most one).
+2605.05219), §3 (objective R), §4 (Theorem 1, Theorem 2, Lemma 1, and the
+plug-in and drift guarantees of Theorems 3 and 4) and §5 (the uniform-spacing
+baseline: gaps that differ by at most one).
 """
 import itertools
 import time
@@ -109,6 +110,47 @@ def test_lemma1_lipschitz():
         assert abs(vp - vq) <= N * tv + 1e-12
 
 
+def _empirical(rng, p, T):
+    """Normalised histogram of T i.i.d. draws of d ~ p on 0..N."""
+    return np.bincount(rng.choice(len(p), size=T, p=p), minlength=len(p)) / T
+
+
+def test_theorem3_plugin_guarantee():
+    """A placement optimal for the empirical distribution p^ of T requests costs,
+    under the true p, at most V(p, M) + 2 N TV(p^, p)."""
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        N = int(rng.integers(2, 40))
+        M = int(rng.integers(1, min(N, 6) + 1))
+        p = rng.random(N + 1) ** 3; p /= p.sum()
+        ph = _empirical(rng, p, int(rng.integers(5, 200)))
+        tv = 0.5 * np.abs(p - ph).sum()
+        _, g_hat = OP.dp_optimum(ph, M)
+        v, _ = OP.dp_optimum(p, M)
+        r = OP.expected_recompute(p, g_hat)
+        assert v - 1e-12 <= r <= v + 2 * N * tv + 1e-12
+
+
+def test_theorem4_drift_guarantee():
+    """Placements recomputed from a sliding window of drifting requests: under the
+    next step's distribution p_T they cost at most V(p_T, M) + 2 N eps, with
+    eps = TV(p_T, window average)."""
+    rng = np.random.default_rng(8)
+    N, M, W = 60, 4, 25
+    a = rng.random(N + 1); a /= a.sum()
+    b = rng.random(N + 1) ** 4; b /= b.sum()
+    steps = 120
+    dists = [(1 - t / steps) * a + (t / steps) * b for t in range(steps + 1)]
+    draws = [rng.choice(N + 1, p=d) for d in dists[:-1]]
+    for T in range(W, steps, 7):
+        window = np.bincount(draws[T - W:T], minlength=N + 1) / W
+        p_next = dists[T]
+        eps = 0.5 * np.abs(p_next - window).sum()
+        _, g_hat = OP.dp_optimum(window, M)
+        v, _ = OP.dp_optimum(p_next, M)
+        assert OP.expected_recompute(p_next, g_hat) <= v + 2 * N * eps + 1e-12
+
+
 # ---- the library's planner against the oracle --------------------------------
 
 @pytest.fixture(scope="module")
@@ -166,6 +208,22 @@ def test_lib_plan_matches_dp_oracle(gdn, N):
             assert len(pos) == M and all(1 <= x <= N for x in pos) and pos == sorted(set(pos))
             # the returned placement reaches the minimum
             assert OP.expected_recompute(p, pos) == pytest.approx(want, rel=1e-9, abs=1e-12 * scale)
+
+
+def test_lib_plan_from_samples_keeps_the_plugin_bound(gdn):
+    """The library's plan built from an empirical distribution obeys Theorem 3
+    under the true distribution (the library's plan and the oracle's optimum may
+    differ among ties, the bound may not)."""
+    rng = np.random.default_rng(9)
+    for _ in range(25):
+        N = int(rng.integers(5, 300))
+        M = int(rng.integers(1, min(N, 16) + 1))
+        p = rng.random(N + 1) ** 2; p /= p.sum()
+        ph = _empirical(rng, p, 400)
+        tv = 0.5 * np.abs(p - ph).sum()
+        pos, _ = gdn.plan_checkpoints(ph, M)
+        v, _ = OP.dp_optimum(p, M)
+        assert OP.expected_recompute(p, pos.tolist()) <= v + 2 * N * tv + 1e-9
 
 
 def test_lib_plan_is_a_brute_force_optimum(gdn):
