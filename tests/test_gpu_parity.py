@@ -173,6 +173,16 @@ def test_full_size_workloads(gdn, name):
                     label=name)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_full_size_tail_on_the_per_token_kernel(gdn, dtype):
+    """The 5% tail replay at full size (16 x 32 pairs, m = 32768, k = 1639) forced
+    onto the exact per-token kernel, with bf16 inputs (bar 3e-3) and float32
+    inputs (bar 1e-5), on sampled pairs."""
+    w = W.tail(device="cuda", dtype=dtype, name=f"tail5_B16_H32_m32768_{dtype}")
+    _check_workload(gdn, w, "recurrent", pairs=_sample_pairs(w, 16, 11), poison=False,
+                    label=f"tail5 per-token {dtype}")
+
+
 def test_grouped_tail_three_layers(gdn):
     """Three linear-attention layers replayed in sequence, each layer's bf16
     outputs being the next layer's q = k = v (identity mixing).  Per layer, the
