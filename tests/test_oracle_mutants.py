@@ -1,0 +1,118 @@
+"""The oracle's pins catch plausible mistakes: each mutant below is the rank-1
+scan with one mistake of the kind a reader of "Tail-Replay: Escaping the Curse
+of Linear Attention in Prefix Caching for Hybrid LLMs" §2.3 eq. (1) could make
+(a dropped or misplaced decay, a wrong sign, a dropped beta, a transposed write,
+the output taken before the update, the key left unnormalised, the state
+recorded before the update).  Every parametrised pin of test_oracle_pins.py is
+run with the mutant in place of the scan, and at least one of them must fail.
+The mistakes are planted here, in CPU test code, never in the oracle."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _load_pins():
+    spec = importlib.util.spec_from_file_location("_pins_for_mutants", os.path.join(HERE, "test_oracle_pins.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _unit(x):
+    x = np.asarray(x, np.float64)
+    n = np.linalg.norm(x, axis=-1, keepdims=True)
+    return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+
+
+def _mutant(step, *, out_before=False, normalize=True, emit_before=False):
+    """A rank-1 scan whose per-token update is ``step(S, a, b, k, v)``."""
+    def scan(S0, q, k, v, alpha, beta, *, normalize_k=True, normalize_q=False, emit_after=()):
+        S = np.array(S0, dtype=np.float64, copy=True)
+        kh = _unit(k) if (normalize_k and normalize) else np.asarray(k, np.float64)
+        qh = None if q is None else (_unit(q) if normalize_q else np.asarray(q, np.float64))
+        v = np.asarray(v, np.float64)
+        emit = set(int(t) for t in emit_after)
+        out = np.zeros((kh.shape[0], S.shape[0])) if qh is not None else None
+        states = {}
+        for t in range(kh.shape[0]):
+            prev = S
+            if emit_before and (t + 1) in emit:
+                states[t + 1] = S.copy()
+            S = step(S, float(alpha[t]), float(beta[t]), kh[t], v[t])
+            if out is not None:
+                out[t] = (prev if out_before else S) @ qh[t]
+            if not emit_before and (t + 1) in emit:
+                states[t + 1] = S.copy()
+        return S, out, states
+    return scan
+
+
+def _ok(S, a, b, k, v):
+    return a * S + np.outer(b * (v - a * (S @ k)), k)
+
+
+MUTANTS = {
+    "correction without decay": _mutant(lambda S, a, b, k, v: a * S + np.outer(b * (v - S @ k), k)),
+    "decay on the write too": _mutant(lambda S, a, b, k, v: a * (S + np.outer(b * (v - S @ k), k))),
+    "wrong sign of the correction": _mutant(lambda S, a, b, k, v: a * S + np.outer(b * (v + a * (S @ k)), k)),
+    "beta dropped from the write": _mutant(lambda S, a, b, k, v: a * S + np.outer(v - a * b * (S @ k), k)),
+    "beta squared": _mutant(lambda S, a, b, k, v: a * S + np.outer(b * b * (v - a * (S @ k)), k)),
+    "transposed write": _mutant(lambda S, a, b, k, v: a * S + np.outer(b * (v - a * (S @ k)), k).T.reshape(S.shape)),
+    # left multiplication only type-checks for a square state
+    "key operator from the left": _mutant(
+        lambda S, a, b, k, v: (a * (np.eye(len(k)) - b * np.outer(k, k)) @ S + b * np.outer(v, k))
+        if S.shape[0] == S.shape[1] else np.full_like(S, np.nan)),
+    "output before the update": _mutant(_ok, out_before=True),
+    "key left unnormalised": _mutant(_ok, normalize=False),
+    "state recorded before the update": _mutant(_ok, emit_before=True),
+}
+
+
+def _form_pins(P):
+    """The pins parametrised by the scan form (the ones a mutant scan can replace)."""
+    names = [n for n in dir(P) if n.startswith("test_")]
+    out = []
+    for n in names:
+        fn = getattr(P, n)
+        marks = getattr(fn, "pytestmark", [])
+        if any(m.name == "parametrize" and m.args and m.args[0] == "form" for m in marks):
+            out.append(fn)
+    return out
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _c_oracle():
+    from oracle.build import build_c_oracle
+    if not oracle.c_oracle_available():
+        build_c_oracle()
+
+
+def test_the_correct_scan_passes_every_pin(monkeypatch):
+    """Control: the same harness with the correct step fails no pin."""
+    P = _load_pins()
+    good = _mutant(_ok)
+    monkeypatch.setattr(P, "_scan", lambda form: good)
+    pins = _form_pins(P)
+    assert len(pins) >= 8
+    for fn in pins:
+        fn("rank1")
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_every_mutant_fails_a_pin(name, monkeypatch):
+    P = _load_pins()
+    monkeypatch.setattr(P, "_scan", lambda form: MUTANTS[name])
+    caught = []
+    for fn in _form_pins(P):
+        try:
+            with np.errstate(all="ignore"):
+                fn("rank1")
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"mutant '{name}' passes every pin"

@@ -254,6 +254,24 @@ def test_rows_independent(form):
     np.testing.assert_allclose(Or, O[:, R], rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("form", FORMS)
+def test_emitted_state_is_the_state_after_that_many_tokens(form):
+    """A checkpoint c holds the state after the c-th token ([SPC] §3): the state
+    emitted after t tokens is the end state of the same scan over the first t
+    tokens only, and the one emitted after the last token is the final state."""
+    rng = np.random.default_rng(13)
+    dk, dv, T = 8, 12, 20
+    q, k, v, a, b = _rand(rng, T, dk, dv)
+    S0 = rng.standard_normal((dv, dk))
+    emit = [1, 2, 7, 20]
+    S, _, st = _scan(form)(S0, q, k, v, a, b, emit_after=emit)
+    assert sorted(st) == emit
+    for t in emit:
+        St, _, _ = _scan(form)(S0, q[:t], k[:t], v[:t], a[:t], b[:t])
+        np.testing.assert_allclose(st[t], St, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(st[T], S)
+
+
 def test_forms_agree_and_emit_prefix_states():
     """literal, rank-1 (numpy) and rank-1 (C) agree; a state emitted after t
     tokens equals the end state of a scan over the first t tokens only."""
