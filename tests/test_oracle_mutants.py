@@ -116,3 +116,72 @@ def test_every_mutant_fails_a_pin(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught.append(fn.__name__)
     assert caught, f"mutant '{name}' passes every pin"
+
+
+# ---- span selection: integer mistakes -----------------------------------------
+
+def _first_at_or_after(positions, depth):
+    for i, c in enumerate(positions, start=1):
+        if int(c) >= int(depth):
+            return i
+    return 0
+
+
+def _strictly_before(positions, depth):
+    j = 0
+    for i, c in enumerate(positions, start=1):
+        if int(c) < int(depth):
+            j = i
+    return j
+
+
+INT_MUTANTS = {
+    "tail length by floor": {"tail_length": lambda m, rn, rd: max(0, min((int(m) * int(rn)) // int(rd), int(m)))},
+    "tail length by float rounding": {"tail_length": lambda m, rn, rd: max(0, min(int(round(m * rn / rd)), int(m)))},
+    "tail span starts one early": {"tail_span": lambda m, rn, rd: (m - oracle.tail_length(m, rn, rd), oracle.tail_length(m, rn, rd))},
+    "tail span one token short": {"tail_span": lambda m, rn, rd: (m - oracle.tail_length(m, rn, rd) + 1, max(0, oracle.tail_length(m, rn, rd) - 1))},
+    "checkpoint strictly before the depth": {"select_checkpoint": _strictly_before},
+    "first checkpoint at or after the depth": {"select_checkpoint": _first_at_or_after},
+    "resume span includes the checkpoint token": {"resume_span": lambda pos, d: (
+        oracle.select_checkpoint(pos, d),
+        (int(pos[oracle.select_checkpoint(pos, d) - 1]) if oracle.select_checkpoint(pos, d) else 0),
+        int(d) - (int(pos[oracle.select_checkpoint(pos, d) - 1]) if oracle.select_checkpoint(pos, d) else 0) + 1)},
+}
+
+
+def _all_pins(P):
+    """Every pin callable here: no arguments, or only the scan form."""
+    import inspect
+    out = []
+    for n in dir(P):
+        if not n.startswith("test_"):
+            continue
+        fn = getattr(P, n)
+        params = list(inspect.signature(fn).parameters)
+        if params == []:
+            out.append((fn, ()))
+        elif params == ["form"]:
+            out.append((fn, ("rank1",)))
+    return out
+
+
+def test_the_correct_span_logic_passes_every_pin():
+    P = _load_pins()
+    pins = _all_pins(P)
+    assert len(pins) >= 15
+    for fn, args in pins:
+        fn(*args)
+
+
+@pytest.mark.parametrize("name", list(INT_MUTANTS))
+def test_every_span_mutant_fails_a_pin(name, monkeypatch):
+    for attr, fn in INT_MUTANTS[name].items():
+        monkeypatch.setattr(oracle, attr, fn)
+    P = _load_pins()
+    caught = []
+    for fn, args in _all_pins(P):
+        try:
+            fn(*args)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"mutant '{name}' passes every pin"
