@@ -5,7 +5,10 @@ of Linear Attention in Prefix Caching for Hybrid LLMs" §2.3 eq. (1) could make
 the output taken before the update, the key left unnormalised, the state
 recorded before the update).  Every parametrised pin of test_oracle_pins.py is
 run with the mutant in place of the scan, and at least one of them must fail.
-The mistakes are planted here, in CPU test code, never in the oracle."""
+The same holds for mistakes in the span selection ([TR] §2.1-§2.2, [SPC] §3:
+the tail length, the replayed range, the checkpoint chosen for a depth).
+The mistakes are planted here, in CPU test code, never in the oracle's files;
+the integer ones replace an oracle function only for the duration of a test."""
 import importlib.util
 import os
 
