@@ -7,6 +7,9 @@ recorded before the update).  Every parametrised pin of test_oracle_pins.py is
 run with the mutant in place of the scan, and at least one of them must fail.
 The same holds for mistakes in the span selection ([TR] §2.1-§2.2, [SPC] §3:
 the tail length, the replayed range, the checkpoint chosen for a depth).
+And for the checkpoint-placement oracle ("Sparse prefix caching for hybrid and
+recurrent LLM serving" §3-§4: the recompute f_g(d), the DP interval costs,
+the balanced gaps), against the pins of test_planner.py.
 The mistakes are planted here, in CPU test code, never in the oracle's files;
 the integer ones replace an oracle function only for the duration of a test."""
 import importlib.util
@@ -185,6 +188,79 @@ def test_every_span_mutant_fails_a_pin(name, monkeypatch):
     for fn, args in _all_pins(P):
         try:
             fn(*args)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"mutant '{name}' passes every pin"
+
+
+# ---- checkpoint placement: mistakes in the planner oracle ---------------------
+
+def _load_planner_pins():
+    spec = importlib.util.spec_from_file_location("_planner_pins_for_mutants", os.path.join(HERE, "test_planner.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _recompute_counting_the_checkpoint(positions, d):
+    if d == 0:
+        return 0
+    best = max([0] + [int(c) for c in positions if int(c) <= d])
+    return d - best + 1
+
+
+def _recompute_strictly_before(positions, d):
+    if d == 0:
+        return 0
+    return d - max([0] + [int(c) for c in positions if int(c) < d])
+
+
+def _interval_cost_off_by_one(p, N):
+    C = np.full((N + 2, N + 2), np.inf)
+    for a in range(N + 1):
+        acc = 0.0
+        C[a][a] = 0.0
+        for b in range(a + 1, N + 2):
+            acc += float(p[b - 1]) * (b - a)
+            C[a][b] = acc
+    return C
+
+
+def _balanced_without_sentinel(N, M):
+    K = M + 1
+    return [((i * N) // K) - (((i - 1) * N) // K) for i in range(1, K + 1)]
+
+
+PLANNER_MUTANTS = {
+    "the checkpoint token is recomputed": {"recompute_len": _recompute_counting_the_checkpoint},
+    "resume only from checkpoints strictly before the depth": {"recompute_len": _recompute_strictly_before},
+    "interval cost counts one token too many": {"_interval_cost": _interval_cost_off_by_one},
+    "balanced gaps sum to N instead of N + 1": {"balanced_gaps": _balanced_without_sentinel},
+}
+
+
+def _argless_pins(P):
+    import inspect
+    return [getattr(P, n) for n in dir(P)
+            if n.startswith("test_") and not inspect.signature(getattr(P, n)).parameters]
+
+
+def test_the_correct_planner_oracle_passes_every_pin():
+    pins = _argless_pins(_load_planner_pins())
+    assert len(pins) >= 8
+    for fn in pins:
+        fn()
+
+
+@pytest.mark.parametrize("name", list(PLANNER_MUTANTS))
+def test_every_planner_mutant_fails_a_pin(name, monkeypatch):
+    from oracle import planner as OPM
+    for attr, fn in PLANNER_MUTANTS[name].items():
+        monkeypatch.setattr(OPM, attr, fn)
+    caught = []
+    for fn in _argless_pins(_load_planner_pins()):
+        try:
+            fn()
         except (AssertionError, ValueError, IndexError):
             caught.append(fn.__name__)
     assert caught, f"mutant '{name}' passes every pin"
