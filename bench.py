@@ -31,19 +31,41 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
 
 
 def measured_traffic(kernel_src: str, profile: str):
-    """HBM bytes per launch from the committed counter summary, or None when the
+    """HBM bytes per launch from the committed counter summary (rocprofv3
+    FETCH_SIZE and WRITE_SIZE runs of this same command, scaled by a copy of
+    known size), with a label naming that source; (None, reason) when the
     kernel source changed since the counters were taken."""
     import hashlib
     try:
         txt = open(profile).read()
         sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
     except OSError:
-        return None
+        return None, "no counter summary"
     vals = dict(l.split(":", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes_per_launch:",
                                                                             "kernel_source_sha256_prefix:")))
+    rel = os.path.relpath(profile, ROOT)
     if vals.get("kernel_source_sha256_prefix", "").strip() != sha:
-        return None
-    return int(vals["traffic_bytes_per_launch"])
+        return None, f"{rel} was taken on another kernel source (sha256 prefix differs from {sha})"
+    return int(vals["traffic_bytes_per_launch"]), (f"{rel}: rocprofv3 FETCH_SIZE / WRITE_SIZE of this command, "
+                                                   f"committed for kernel source sha256 prefix {sha}; "
+                                                   "not measured in this run")
+
+
+def host_cpu():
+    """Logical CPUs of the host, those this process may use, and the CPU model."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": usable, "logical_cpus": os.cpu_count(), "model": model}
 
 
 def algorithmic_bytes(token_heads: int, pairs: int, dk: int, dv: int, elem: int,
@@ -93,7 +115,9 @@ def cpu_baseline(w, spans, budget_s: float = 15.0):
     n = min(n, len(allp))
     dt, toks = run(allp[:n])
     rate = toks / H / dt  # token-heads / H = tokens with all heads
+    cpu = host_cpu()
     return {"value": rate, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "nproc": cpu["nproc"], "logical_cpus": cpu["logical_cpus"], "cpu_model": cpu["model"],
             "sample": f"{n} of {len(allp)} (request, head) pairs, {spans[0][1]} tokens each, "
                       f"fp64 C rank-1 oracle with OpenMP; {dt:.1f} s wall"}
 
@@ -424,9 +448,12 @@ def main():
         roof = {"bound": "alu", "achieved": nflops / (kern_ms * 1e-3) / 1e12,
                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = (measured_traffic(os.path.join(ROOT, "gated_delta_rule_scan_amd", "csrc", "gdn_chunked.hip"),
-                                        os.path.join(ROOT, "profiles", "chunked_kernel_tail5pct_traffic.md"))
-                       if chunked and o is not None else None)
+    if chunked and o is not None:
+        roof["traffic"], roof["traffic_source"] = measured_traffic(
+            os.path.join(ROOT, "gated_delta_rule_scan_amd", "csrc", "gdn_chunked.hip"),
+            os.path.join(ROOT, "profiles", "chunked_kernel_tail5pct_traffic.md"))
+    else:
+        roof["traffic"], roof["traffic_source"] = None, "no counter summary for this kernel configuration"
     roof["algorithmic_bytes_per_launch"] = nbytes
     roof["algorithmic_flops_per_launch"] = nflops
     roof["kernel_ms"] = kern_ms

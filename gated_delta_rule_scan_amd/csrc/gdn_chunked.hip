@@ -100,16 +100,14 @@ struct Smem {
     alignas(16) _Float16 qh[2][C * KS];  // q^ (or q / 2^E), fp16 (same layout)
     alignas(16) uint16_t kqr[2][C * DK];  // raw bf16 keys, queries of the chunk after next: [token][column]
     alignas(16) uint16_t vr[NVB][NW][C * 32];  // raw bf16 v: [wave][token][32 value columns]
-    alignas(16) _Float16 tT[C * C];      // (T diag(beta))^T * 2^eT, row s, column t
+    alignas(16) _Float16 tT[2][C * C];   // (T diag(beta))^T * 2^eT as fp16 hi [0] + lo [1], row s, column t
     alignas(16) _Float16 pT[2][C * C];   // P^T, row s, column t
-    alignas(16) float gl[2][C];          // chunk-local prefix sum of log2 alpha
+    alignas(16) float gl[2][C];          // chunk-local prefix sum of log2 alpha (gl[C-1]: the chunk's total)
     alignas(16) float be[2][C];          // beta (0 past the chunk)
-    alignas(16) float eg[2][C];          // 2^{g_t}
-    alignas(16) float ws[2][C];          // 2^{g_C - g_t}
+    alignas(16) float ks[2][C];          // 1 / ||k'_t||: scale of the stored key row k'_t (0 past the chunk)
     alignas(16) float kq[2][C];          // 1, or 2^{E_t} for unnormalised queries
     alignas(16) float cw[NW][4][C];      // per-wave coefficients (see the state side)
-    alignas(16) float4 tpart[3][64];     // T_00, T_11^T, A_10^T tiles (accumulator layout) per lane
-    float gC[2];
+    alignas(16) float4 tpart[2][64];     // T_00, T_11^T tiles (accumulator layout) per lane
     float tsc;                           // 2^{-eT}
 };
 constexpr uint32_t OFF_KH = offsetof(Smem, kh);
@@ -120,6 +118,7 @@ constexpr uint32_t OFF_TT = offsetof(Smem, tT);
 constexpr uint32_t OFF_PT = offsetof(Smem, pT);
 constexpr uint32_t OFF_CW = offsetof(Smem, cw);
 static_assert(OFF_QH == OFF_KH + 2 * KBUF, "query tiles follow the key tiles");
+static_assert(sizeof(Smem) <= 81920, "two workgroups must share a CU's 160 KiB of LDS");
 
 // ---- LDS layouts -------------------------------------------------------------
 // Key/query tiles: token t occupies row krow(t) (272 bytes, so row r starts at
@@ -458,9 +457,67 @@ __device__ __forceinline__ void dma_v_all(uint32_t sm_lds, int vb, const Bases &
                   sm_lds + OFF_VR + (uint32_t)(((vb * NW + w2) * C * 32 + 16 * k * 32) * 2));
 }
 
-// ---- key side, part 1 (all waves): fp16 unit keys / queries and gate sums -----
-// Converts the 8 columns of one lane (16-byte unit pair of its row) and stores
-// them at LDS byte offset dst (the row's lower unit; the upper one is +16).
+// ---- key side, part 1 (all waves): fp16 keys / queries and gate sums -------------
+// Keys are kept as stored: a bf16 row is exact in fp16 (8 significant bits)
+// when its elements lie in the fp16 range, and the normalisation 1/||k|| goes
+// into per-token coefficients (ks) instead of being rounded into the row.
+// Converts the 8 columns of one lane (16-byte unit pair of its row) and
+// stores them at LDS byte offset dst (the row's lower unit; the upper one is
+// +16); returns the row's scale s with k^ = s k' (k' the stored fp16 row),
+// 0 for rows past the chunk.
+__device__ __forceinline__ float convert_key_row(Smem &sm, uint32_t dst, uint4 raw, bool live) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = bflo(wd[e]);
+        f[2 * e + 1] = bfhi(wd[e]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16x2v pr = __builtin_bit_cast(bf16x2v, wd[e]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+    }
+    ss = row16_sum(ss);  // one token row per 16 lanes
+    float s = live ? __builtin_amdgcn_rsqf(ss) : 0.f;
+    // A row with ||k|| in [1/2, 2) is stored as it is (unit keys always are).
+    // Any other row sends the wave through the general form: the row is scaled
+    // by the power of two that brings its largest element into [1/2, 1)
+    // (exact), so that it fits fp16 and its squared norm lies in [1/4, d_k];
+    // this also covers squared norms that overflow or underflow float32.  A
+    // zero row keeps scale 0 (it stays zero).
+    if (__builtin_amdgcn_ballot_w64(live && !(ss >= 0.25f && ss < 4.f)) != 0) {
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+        mx = row16_max(mx);
+        const int E = __builtin_amdgcn_frexp_expf(mx);  // mx = m 2^E, m in [1/2, 1)
+        float s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f[e] = __builtin_amdgcn_ldexpf(f[e], -E);
+            s2 = fmaf(f[e], f[e], s2);
+        }
+        s2 = row16_sum(s2);
+        s = (live && s2 > 0.f) ? __builtin_amdgcn_rsqf(s2) : 0.f;
+    }
+    half4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = (_Float16)f[e];
+        hi[e] = (_Float16)f[4 + e];
+    }
+    lds_st(sm, dst, lo);
+    lds_st(sm, dst + 16, hi);
+    return s;
+}
+
+// Queries: converts the 8 columns of one lane as convert_key_row does, either
+// normalised (NORMALISE: q / ||q||, rounded to fp16) or scaled by the power of
+// two 2^-E that brings the row's largest element into [1/2, 1), with 2^E
+// returned in kq_out.
 template <bool NORMALISE>
 __device__ __forceinline__ void convert_row(Smem &sm, uint32_t dst, uint4 raw, bool live, float *kq_out) {
     // rows past the chunk hold a copy of a live row (finite); they get scale 0
@@ -481,8 +538,28 @@ __device__ __forceinline__ void convert_row(Smem &sm, uint32_t dst, uint4 raw, b
             ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
         }
         ss = row16_sum(ss);  // one token row per 16 lanes
-        // a key of squared norm below 1e-36 is treated as zero
-        sc = (live && ss > 1e-36f) ? __builtin_amdgcn_rsqf(ss) : 0.f;
+        sc = live ? __builtin_amdgcn_rsqf(ss) : 0.f;
+        // The squared norm of a bf16 row can overflow float32 (||q|| above
+        // ~1.8e19) or underflow it (tiny rows; a zero row gives 0).  Any row
+        // outside [2^-100, 2^100] sends the wave through the exact form: the
+        // row is first scaled by a power of two that brings its largest
+        // element into [1/2, 1), so its squared norm lies in [1/4, d_k] and
+        // 1/||q|| is exact to rounding; a zero row keeps scale 0 (stays zero).
+        if (__builtin_amdgcn_ballot_w64(live && !(ss >= 0x1p-100f && ss <= 0x1p100f)) != 0) {
+            float mx = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+            mx = row16_max(mx);
+            const int E = __builtin_amdgcn_frexp_expf(mx);  // mx = m 2^E, m in [1/2, 1)
+            float s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f[e] = __builtin_amdgcn_ldexpf(f[e], -E);
+                s2 = fmaf(f[e], f[e], s2);
+            }
+            s2 = row16_sum(s2);
+            sc = (live && s2 > 0.f) ? __builtin_amdgcn_rsqf(s2) : 0.f;
+        }
     } else {
         float mx = 0.f;
 #pragma unroll
@@ -537,7 +614,8 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
         const bool live = t < lc;
         const uint32_t dst = (kind ? qbuf : kbuf) + L.cvt + (uint32_t)(((rb & 3) + 16 * (rb >> 2)) * KROWB);
         if (kind == 0) {
-            convert_row<true>(sm, dst, raw[gi], live, nullptr);
+            const float ksv = convert_key_row(sm, dst, raw[gi], live);
+            if (L.n16 == 0) sm.ks[pb][t] = ksv;
         } else {
             float kqv = 1.f;
             convert_row<NORM_Q>(sm, dst, raw[gi], live, &kqv);
@@ -551,15 +629,11 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
         const float av = bf(pf.ga);
         const float lg = live ? log2_(fmaxf(av, 1e-30f)) : 0.f;
         const float gs = scan32(lg);
-        const float gC = lane_val(gs, C - 1);
         if (L.lane < 32) {
             sm.gl[pb][tl] = gs;
-            sm.eg[pb][tl] = exp2_(gs);
-            sm.ws[pb][tl] = exp2_(gC - gs);
         } else {
             sm.be[pb][tl] = live ? bf(pf.gb) : 0.f;
         }
-        if (L.lane == 0) sm.gC[pb] = gC;
     }
 }
 
@@ -589,9 +663,32 @@ __device__ __forceinline__ void task_frags(const Smem &sm, uint32_t buf, uint32_
     for (int ks = 0; ks < 4; ++ks) f[ks] = lds_ld<half8>(sm, buf + base + 16 * ks);
 }
 
+// fp16 hi/lo pair of float32 values: x = hi + lo to about 2^-22 relative.
+__device__ __forceinline__ void split16(const floatx4 &x, half4 &hi, half4 &lo) {
+    hi = h4(x);
+    floatx4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = x[j] - (float)hi[j];
+    lo = h4(r);
+}
+__device__ __forceinline__ floatx4 f4(half4 x) {
+    floatx4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (float)x[j];
+    return r;
+}
+
 // Diagonal tile b (tokens 16b .. 16b+15), wave 0 (b = 0) or wave 2 (b = 1):
 // T_bb, returned for b = 0 as T_00 and for b = 1 as T_11^T (both in
 // accumulator layout: lane i holds rows 4(i/16) + j, column i%16).
+//
+// The product form gives a first inverse T0 = R - R L R (R the 8 x 8
+// block-diagonal inverse, L the lower-left block); its fp16 intermediates lose
+// accuracy when the keys of the tile are nearly parallel and beta approaches
+// 2 (entries of N^2, N^4 far above those of the inverse).  One Newton step,
+//     T1 = T0 + T0 E,   E = I - (I + A) T0,
+// with A (float32) applied as an fp16 hi/lo pair and T0 exact in fp16,
+// squares the relative error of T0.
 __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, const Lane &L) {
     const int c = L.n16, rb = 4 * L.g;
     half8 f[4];
@@ -602,15 +699,23 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
     for (int ks = 0; ks < 4; ++ks) G = mfma16(f[ks], f[ks], G);
     const float *gl = sm.gl[pb];
     const float *be = sm.be[pb];
+    const float *kn = sm.ks[pb];
     half4 id4;
+    floatx4 idf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) id4[j] = (_Float16)(rb + j == c ? 1.f : 0.f);
+    for (int j = 0; j < 4; ++j) {
+        id4[j] = (_Float16)(rb + j == c ? 1.f : 0.f);
+        idf[j] = rb + j == c ? 1.f : 0.f;
+    }
     // A (rows > cols) and A^T (rows < cols) of the tile, split into the two
-    // 8 x 8 diagonal blocks (N) and the lower-left block (L)
-    const float gls = gl[16 * b + c], bes = be[16 * b + c];
+    // 8 x 8 diagonal blocks (N) and the lower-left block (L); the stored keys
+    // k' carry their scales ks (k^ = ks k')
+    const float gls = gl[16 * b + c], bes = be[16 * b + c], kss = kn[16 * b + c];
     const float4 glt = *reinterpret_cast<const float4 *>(&gl[16 * b + rb]);
     const float4 bet = *reinterpret_cast<const float4 *>(&be[16 * b + rb]);
+    const float4 knt = *reinterpret_cast<const float4 *>(&kn[16 * b + rb]);
     const float glv[4] = {glt.x, glt.y, glt.z, glt.w}, bev[4] = {bet.x, bet.y, bet.z, bet.w};
+    const float knv[4] = {knt.x, knt.y, knt.z, knt.w};
     floatx4 N, Nt, Lw, Lt;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -619,7 +724,7 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
         const float d = glv[j] - gls;
         // computed on every lane (the diagonal is dropped by the selects), so
         // that no branch splits the task
-        const float val = (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * G[j];
+        const float val = (lower ? bev[j] : bes) * exp2_(lower ? d : -d) * (knv[j] * kss) * G[j];
         N[j] = (lower && same8) ? val : 0.f;
         Nt[j] = (upper && same8) ? val : 0.f;
         Lw[j] = (lower && !same8) ? val : 0.f;
@@ -635,14 +740,36 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
     const floatx4 R1t = mm16(id4 - Nh, id4 + N2th, z);  // (I - N^T)(I + (N^2)^T)
     const floatx4 R = mm16(id4 + h4(N4t), h4(R1), z);   // (I + N^4) R1 = blockdiag inverse
     const floatx4 Rt = mm16(id4 + h4(N4), h4(R1t), z);  // its transpose
+    // T0 and T0^T (accumulator layout), R - R L R
+    floatx4 T0, T0t;
     if (b == 0) {
-        // T_00 = R - R (L R)
-        const floatx4 X = mm16(Lth, h4(R), z);
-        return mm16(h4(Rt), -h4(X), R);
+        const half4 X = h4(mm16(Lth, h4(R), z));  // L R
+        T0 = mm16(h4(Rt), -X, R);
+        T0t = mm16(X, -h4(Rt), Rt);
+    } else {
+        const half4 Xt = h4(mm16(Lh, h4(Rt), z));  // (R L)^T
+        T0t = mm16(h4(R), -Xt, Rt);
+        T0 = mm16(Xt, -h4(R), R);
     }
-    // T_11^T = R^T - R^T (L^T R^T)
-    const floatx4 Xt = mm16(Lh, h4(Rt), z);
-    return mm16(h4(R), -h4(Xt), Rt);
+    const half4 T0h = h4(T0), T0th = h4(T0t);
+    // The two copies of T0 come from separate chains (their roundings
+    // differ), so the residual is taken against the copy the step starts
+    // from; the error of T1 is then the product of the two copies' errors.
+    half4 Ah, Al;
+    if (b == 0) {
+        // T1 = T0 + T0' E, E = I - T0 - A T0 (A = A_hi + A_lo; the A operand of A T0 is A^T)
+        split16(Nt + Lt, Ah, Al);
+        floatx4 AT = mm16(Ah, T0h, z);
+        AT = mm16(Al, T0h, AT);
+        const half4 Eh = h4(idf - f4(T0h) - AT);
+        return mm16(T0th, Eh, f4(T0h));
+    }
+    // T1^T = T0^T + T0'^T E^T, E^T = I - T0^T - A^T T0^T (the left residual I - T0 (I + A), transposed)
+    split16(N + Lw, Ah, Al);
+    floatx4 AT = mm16(Ah, T0th, z);
+    AT = mm16(Al, T0th, AT);
+    const half4 Eh = h4(idf - f4(T0th) - AT);
+    return mm16(T0h, Eh, f4(T0th));
 }
 
 // Wave 3: A_10^T (accumulator layout) from the (0, 1) Gram tile.
@@ -655,24 +782,38 @@ __device__ __forceinline__ floatx4 key_side_a10t(const Smem &sm, int pb, const L
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) G01 = mfma16(f0[ks], f1[ks], G01);  // (k_r . k_{16+c})
     const float *gl = sm.gl[pb];
-    const float gt = gl[16 + c], bt = sm.be[pb][16 + c];
+    const float gt = gl[16 + c], bt = sm.be[pb][16 + c] * sm.ks[pb][16 + c];
     const float4 gs4 = *reinterpret_cast<const float4 *>(&gl[rb]);
-    const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+    const float4 ks4 = *reinterpret_cast<const float4 *>(&sm.ks[pb][rb]);
+    const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w}, ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
     floatx4 A10t;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) A10t[j] = bt * exp2_(gt - gsv[j]) * G01[j];
+    for (int j = 0; j < 4; ++j) A10t[j] = bt * exp2_(gt - gsv[j]) * ksv[j] * G01[j];
     return A10t;
 }
 
 // Combine (one wave): T_10 = -T_11 A_10 T_00, then T diag(beta) scaled into
-// the fp16 band and stored as (row s, column t).
-__device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L) {
+// the fp16 band and stored as an fp16 hi/lo pair (row s, column t).  Both
+// products take their operands as hi/lo pairs (three MFMAs each: hi hi,
+// lo hi, hi lo), so that T keeps float32 accuracy up to the state update.
+// A10t: A_10^T of the chunk, kept in this wave's registers since its task.
+__device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L, const floatx4 &A10t) {
     const int lane = L.lane;
-    const float4 a = sm.tpart[0][lane], bq = sm.tpart[1][lane], cq = sm.tpart[2][lane];
-    const floatx4 T00 = {a.x, a.y, a.z, a.w}, T11t = {bq.x, bq.y, bq.z, bq.w}, A10t = {cq.x, cq.y, cq.z, cq.w};
+    const float4 a = sm.tpart[0][lane], bq = sm.tpart[1][lane];
+    const floatx4 T00 = {a.x, a.y, a.z, a.w}, T11t = {bq.x, bq.y, bq.z, bq.w};
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-    const floatx4 W = mm16(h4(A10t), h4(T00), z);
-    const floatx4 T10 = mm16(h4(T11t), -h4(W), z);
+    half4 ah, al, th, tl;
+    split16(A10t, ah, al);
+    split16(T00, th, tl);
+    floatx4 W = mm16(ah, th, z);  // A_10 T_00
+    W = mm16(al, th, W);
+    W = mm16(ah, tl, W);
+    half4 wh, wl, uh, ul;
+    split16(-W, wh, wl);
+    split16(T11t, uh, ul);
+    floatx4 T10 = mm16(uh, wh, z);  // -T_11 (A_10 T_00)
+    T10 = mm16(ul, wh, T10);
+    T10 = mm16(uh, wl, T10);
     const int c = L.n16, rb = 4 * L.g;
     const float *be = sm.be[pb];
     const float bs0 = be[c];
@@ -694,11 +835,19 @@ __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L
         t10 *= sc;
         t11 *= sc;
     }
-    _Float16 *tt = sm.tT;
-    *reinterpret_cast<half4 *>(&tt[c * C + rb]) = h4(t00);        // t = rb + j, s = c
-    *reinterpret_cast<half4 *>(&tt[c * C + 16 + rb]) = h4(t10);   // t = 16 + rb + j, s = c
+    half4 h00, l00, h10, l10, h11, l11;
+    split16(t00, h00, l00);
+    split16(t10, h10, l10);
+    split16(t11, h11, l11);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tt[(16 + rb + j) * C + 16 + c] = (_Float16)t11[j];  // t = 16 + c, s = 16 + rb + j
+    for (int part = 0; part < 2; ++part) {
+        _Float16 *tt = sm.tT[part];
+        const half4 x00 = part ? l00 : h00, x10 = part ? l10 : h10, x11 = part ? l11 : h11;
+        *reinterpret_cast<half4 *>(&tt[c * C + rb]) = x00;        // t = rb + j, s = c
+        *reinterpret_cast<half4 *>(&tt[c * C + 16 + rb]) = x10;   // t = 16 + rb + j, s = c
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tt[(16 + rb + j) * C + 16 + c] = x11[j];  // t = 16 + c, s = 16 + rb + j
+    }
     if (lane == 0) sm.tsc = ldexpf(1.f, -eT);
 }
 
@@ -720,6 +869,7 @@ __device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
     }
     const float *gl = sm.gl[pb];
     const float g0 = gl[c], g1 = gl[16 + c];
+    const float ks0 = sm.ks[pb][c], ks1 = sm.ks[pb][16 + c];  // scales of the stored keys s = c, 16 + c
     const float4 a4 = *reinterpret_cast<const float4 *>(&gl[rb]);
     const float4 b4 = *reinterpret_cast<const float4 *>(&gl[16 + rb]);
     const float gt0[4] = {a4.x, a4.y, a4.z, a4.w}, gt1[4] = {b4.x, b4.y, b4.z, b4.w};
@@ -727,9 +877,9 @@ __device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = rb + j;
-        const float e00 = exp2_(gt0[j] - g0) * P00[j], e11 = exp2_(gt1[j] - g1) * P11[j];
+        const float e00 = exp2_(gt0[j] - g0) * ks0 * P00[j], e11 = exp2_(gt1[j] - g1) * ks1 * P11[j];
         x00[j] = c <= r ? e00 : 0.f;
-        x10[j] = exp2_(gt1[j] - g0) * P10[j];
+        x10[j] = exp2_(gt1[j] - g0) * ks0 * P10[j];
         x11[j] = c <= r ? e11 : 0.f;
     }
     _Float16 *pt = sm.pT[pb];
@@ -739,23 +889,20 @@ __device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
 }
 
 // Key-side tasks of one chunk after its conversion: wave 0 tile 0, wave 2
-// tile 1, wave 3 A_10^T (kept for the combine), wave 1 P.
+// tile 1, wave 3 A_10^T (kept in its registers, a10t, for its own combine),
+// wave 1 P.
 template <bool WANT_O>
-__device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, const Lane &L) {
+__device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, const Lane &L, floatx4 &a10t) {
     if (w == 1) {
         if (WANT_O) key_side_P(sm, pb, L);
         return;
     }
-    floatx4 r;
-    int slot;
     if (w == 3) {
-        r = key_side_a10t(sm, pb, L);
-        slot = 2;
-    } else {
-        r = key_side_tile(sm, pb, w >> 1, L);
-        slot = w >> 1;
+        a10t = key_side_a10t(sm, pb, L);
+        return;
     }
-    sm.tpart[slot][L.lane] = make_float4(r[0], r[1], r[2], r[3]);
+    const floatx4 r = key_side_tile(sm, pb, w >> 1, L);
+    sm.tpart[w >> 1][L.lane] = make_float4(r[0], r[1], r[2], r[3]);
 }
 
 // ---- state-side operand reads ---------------------------------------------------
@@ -905,7 +1052,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     // The upper-right 16x16 blocks of T^T and P^T (s >= 16, t < 16) stay zero.
     for (int idx = tid; idx < 16 * 16; idx += NT) {
         const int o = (16 + (idx >> 4)) * C + (idx & 15);
-        sm.tT[o] = (_Float16)0.f;
+        sm.tT[0][o] = sm.tT[1][o] = (_Float16)0.f;
         sm.pT[0][o] = sm.pT[1][o] = (_Float16)0.f;
     }
 
@@ -915,6 +1062,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     cur.lc = len > 0 ? chunk_len(P, len, 0, cur.ne, ne_end) : 0;
     Chunk nx = next_chunk(P, cur, len, ne_end);
     Pref pf;
+    floatx4 a10t = {0.f, 0.f, 0.f, 0.f};  // wave 3 (key side): A_10^T of the chunk whose T is combined next
     int vb = 0;  // V buffer of the current chunk
     // With q = k = v (ALIAS) a chunk's rows are copied once, into raw tile
     // (chunk index % 2), and serve as keys, queries and values until the
@@ -937,7 +1085,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L, ALIAS ? RAW1 : OFF_KQR);
             load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
         }
-        if (KEY) key_side_tasks<WANT_O>(sm, 0, w, L);
+        if (KEY) key_side_tasks<WANT_O>(sm, 0, w, L, a10t);
     }
 
     int p = 0;   // key-side buffer of the current chunk
@@ -1009,13 +1157,16 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         }
         const float isg = exp2_(-sigma);
         if (lane < 32) {
-            const float e = sm.eg[p][lane];
+            const float glt = sm.gl[p][lane];
+            const float e = exp2_(glt);          // 2^{g_t}
             const float kq = NORM_Q ? 1.f : sm.kq[p][lane];
-            cwl[lane] = e * isg;                 // B~ = v - cw0 Y
+            const float kst = sm.ks[p][lane];    // k^_t = kst k'_t
+            cwl[lane] = e * isg * kst;           // B~ = v - cw0 Y', Y' = K' Sacc^T
             if (WANT_O) cwl[C + lane] = kq * e * isg;  // o (state part) = cw1 Z
-            // W' = cw2 U and o (intra part) = cw3 (P U'), for unscaled T, B~, U
-            // and no rescale of the state (rewritten below otherwise)
-            cwl[2 * C + lane] = sm.ws[p][lane] * exp2_(sigma - sm.gC[p]);
+            // W' = cw2 U (rows of K'^T W' = K^^T W) and o (intra part) = cw3 (P U'),
+            // for unscaled T, B~, U and no rescale of the state (rewritten below
+            // otherwise): 2^{g_C - g_t} 2^{sigma - g_C} kst
+            cwl[2 * C + lane] = exp2_(sigma - glt) * kst;
             if (WANT_O && !NORM_Q) cwl[3 * C + lane] = kq;
         }
         // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
@@ -1052,7 +1203,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             // the last T step is on the critical path of this phase: it takes
             // issue priority over the co-resident workgroup's waves
             __builtin_amdgcn_s_setprio(2);
-            key_side_combine(sm, p, L);
+            key_side_combine(sm, p, L, a10t);
             __builtin_amdgcn_s_setprio(0);
         }
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
@@ -1065,7 +1216,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
                 dma_v_all(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L);
             }
             if (w != 3) __builtin_amdgcn_s_setprio(1);  // the longer tasks of this phase go first
-            if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L);
+            if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L, a10t);
             if (w != 3) __builtin_amdgcn_s_setprio(0);
             if (!EARLY) load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
         };
@@ -1074,19 +1225,24 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         // operands of `cur` that are complete now are read before the tasks
         const half8 tfr0 = tr_frag_st(sm, OFF_TT, 0, L);
         const half8 tfr1 = tr_frag_st(sm, OFF_TT, 1, L);
+        const half8 tfl0 = tr_frag_st(sm, OFF_TT + C * C * 2, 0, L);  // lo part of T
+        const half8 tfl1 = tr_frag_st(sm, OFF_TT + C * C * 2, 1, L);
         half8 pfr0, pfr1;
         if (WANT_O) {
             pfr0 = tr_frag_st(sm, OFF_PT + p * (C * C * 2), 0, L);
             pfr1 = tr_frag_st(sm, OFF_PT + p * (C * C * 2), 1, L);
         }
         const float tsc = sm.tsc;
-        const float gCp = sm.gC[p];
+        const float gCp = sm.gl[p][C - 1];
         if (!SPLIT) key_phase();
 
-        // U = (T diag(beta)) B~
+        // U = (T diag(beta)) B~, T as its hi/lo pair
         floatx16 U = {};
-        U = mfma32(tfr0, to_frag(Y, 0), U);
-        U = mfma32(tfr1, to_frag(Y, 1), U);
+        const half8 yf0 = to_frag(Y, 0), yf1 = to_frag(Y, 1);
+        U = mfma32(tfr0, yf0, U);
+        U = mfma32(tfr1, yf1, U);
+        U = mfma32(tfl0, yf0, U);
+        U = mfma32(tfl1, yf1, U);
         // K^T fragments of the state update
         half8 ktf[4][2];
 #pragma unroll
@@ -1137,7 +1293,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         const bool scaled = tsc != 1.f || eB != 0 || eU != 0 || delta != 0.f;
         if (scaled && lane < 32) {
             // W' = cw2 U, cw2 = 2^{g_C - g_t} 2^sig1 us as one power of two
-            cwl[2 * C + lane] = exp2_(fminf(sm.gC[p] - sm.gl[p][lane] + sig1 + lus, 126.f));
+            cwl[2 * C + lane] = exp2_(fminf(gCp - sm.gl[p][lane] + sig1 + lus, 126.f)) * sm.ks[p][lane];
             if (WANT_O) cwl[3 * C + lane] = (NORM_Q ? 1.f : sm.kq[p][lane]) * exp2_(lus - (float)eU);  // o (intra) = cw3 (P U')
         }
 

@@ -169,11 +169,18 @@ gdn_status set_state_out(std::vector<Work> &work, float *state_out, const gdn_sh
 
 bool misaligned(const void *p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-// Validate pointers, pick the kernel and queue the launches.
-gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
-               const void *alpha, const void *beta, void *o,
-               const float *init_base, float *emit_base, int32_t M,
-               const std::vector<Work> &work, hipStream_t stream) {
+// A validated call: the kernel to run and the launch descriptor's common part.
+struct Plan {
+    bool chunked = false;
+    gdn::Elem elem = gdn::Elem::BF16;
+    gdn::LaunchDesc d;
+};
+
+// Validate pointers and alignment and pick the kernel; nothing is queued.
+gdn_status validate(const gdn_shape *s, const void *q, const void *k, const void *v,
+                    const void *alpha, const void *beta, void *o,
+                    const float *init_base, float *emit_base, int32_t M,
+                    const std::vector<Work> &work, Plan *plan) {
     bool any_tokens = false;
     for (const Work &w : work) any_tokens |= w.len > 0;
     if (any_tokens) {
@@ -203,10 +210,10 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
                     "GDN_KERNEL_CHUNKED: no chunked kernel for d_k = %d, d_v = %d, dtype %d, flags 0x%x "
                     "(it needs bf16, d_k = d_v = 128 and GDN_NORMALIZE_K)",
                     s->dk, s->dv, s->dtype, s->flags);
-    const gdn::Elem elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
-    const bool chunked = kern == 1;
+    plan->elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
+    plan->chunked = kern == 1;
 
-    gdn::LaunchDesc d;
+    gdn::LaunchDesc &d = plan->d;
     std::memset(&d, 0, sizeof(d));
     d.q = q;
     d.k = k;
@@ -220,9 +227,15 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
     d.flags = (int32_t)(s->flags & (GDN_NORMALIZE_K | GDN_NORMALIZE_Q));
     // one tensor for q, k and v (a layer fed its predecessor's outputs): the
     // chunked kernel then reads each row once
-    if (chunked && k && k == v && s->dk == s->dv && (!o || q == k)) d.flags |= gdn::kAliasQKV;
+    if (plan->chunked && k && k == v && s->dk == s->dv && (!o || q == k)) d.flags |= gdn::kAliasQKV;
     d.M = M;
+    return GDN_OK;
+}
 
+// Queue the launches of a validated call (several when the work items or
+// their emissions exceed one descriptor).
+gdn_status launch(const gdn_shape *s, Plan &plan, const std::vector<Work> &work, hipStream_t stream) {
+    gdn::LaunchDesc &d = plan.d;
     size_t i = 0;
     while (i < work.size()) {
         int nreq = 0, nemit = 0;
@@ -248,12 +261,23 @@ gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
         if (nreq == 0)  // cannot happen: one request never exceeds the emission budget
             return fail(GDN_ERR_UNSUPPORTED, "emission list does not fit one launch");
         d.nreq = nreq;
-        hipError_t err = chunked ? gdn::launch_chunked(d, s->dk, s->dv, elem, stream)
-                                 : gdn::launch_recurrent(d, s->dk, s->dv, elem, stream);
+        hipError_t err = plan.chunked ? gdn::launch_chunked(d, s->dk, s->dv, plan.elem, stream)
+                                      : gdn::launch_recurrent(d, s->dk, s->dv, plan.elem, stream);
         if (err != hipSuccess)
             return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     }
     return GDN_OK;
+}
+
+// Validate, then queue the launches.
+gdn_status run(const gdn_shape *s, const void *q, const void *k, const void *v,
+               const void *alpha, const void *beta, void *o,
+               const float *init_base, float *emit_base, int32_t M,
+               const std::vector<Work> &work, hipStream_t stream) {
+    Plan plan;
+    const gdn_status st = validate(s, q, k, v, alpha, beta, o, init_base, emit_base, M, work, &plan);
+    if (st != GDN_OK) return st;
+    return launch(s, plan, work, stream);
 }
 
 int64_t tail_len_exact(int64_t m, int64_t r_num, int64_t r_den) {
@@ -368,15 +392,17 @@ GDN_API gdn_status gdn_tail_replay_with_h2d(const gdn_shape *shape, const void *
     if (kv_bytes > 0 && (!kv_dst || !kv_src))
         return fail(GDN_ERR_INVALID_ARGUMENT, "kv_dst or kv_src is NULL with kv_bytes = %zu", kv_bytes);
     if (!copy_done) return fail(GDN_ERR_INVALID_ARGUMENT, "copy_done is NULL");
+    // every argument of the replay is checked before anything is queued
+    Plan plan;
+    if (shape->B > 0 &&
+        (st = validate(shape, q, k, v, alpha, beta, o, nullptr, nullptr, 0, work, &plan)) != GDN_OK)
+        return st;
     // the transfer goes first, so that the copy engine starts while the replay is queued
     hipError_t e = hipSuccess;
     if (kv_bytes > 0) e = hipMemcpyAsync(kv_dst, kv_src, kv_bytes, hipMemcpyHostToDevice, copy_stream);
     if (e == hipSuccess) e = hipEventRecord(copy_done, copy_stream);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "transfer: %s", hipGetErrorString(e));
-    if (shape->B > 0) {
-        st = run(shape, q, k, v, alpha, beta, o, nullptr, nullptr, 0, work, stream);
-        if (st != GDN_OK) return st;
-    }
+    if (shape->B > 0 && (st = launch(shape, plan, work, stream)) != GDN_OK) return st;
     // work queued on `stream` after this call sees both the replayed states and the transfer
     e = hipStreamWaitEvent(stream, copy_done, 0);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "join: %s", hipGetErrorString(e));

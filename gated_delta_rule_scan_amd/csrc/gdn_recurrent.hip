@@ -50,6 +50,15 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Maximum over 16 aligned lanes of non-negative values (every lane receives it).
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return x;
+}
+
 template <int DK, int DV, int DVB, typename T>
 __global__ __launch_bounds__(kLanesPerRow * DVB, 4)  // four waves per SIMD
 void recurrent_kernel(const LaunchDesc P)
@@ -198,30 +207,40 @@ void recurrent_kernel(const LaunchDesc P)
             xa = to_f32(ag[ab]);
             xb = to_f32(bg[ab]);
         }
+        // A row that is normalised is stored scaled by the power of two that
+        // brings its largest element into [1/2, 1) (exact), so that its sum of
+        // squares lies in [1/4, d] and neither overflows (||x|| above ~1.8e19
+        // in float32) nor underflows; the stored scale is 1/||scaled row||, and
+        // a zero row keeps scale 0.
+        auto stage_row = [&](const float (&x)[CPT], bool live, bool norm, float *dst, float *scale_out) {
+            float y[CPT];
+            int E = 0;
+            if (norm) {
+                float mx = 0.f;
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) mx = fmaxf(mx, live ? fabsf(x[i]) : 0.f);
+                E = __builtin_amdgcn_frexp_expf(row16_max(mx));
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                y[i] = live ? __builtin_amdgcn_ldexpf(x[i], -E) : 0.f;
+                dst[kPPT * i] = y[i];
+                ss = fmaf(y[i], y[i], ss);
+            }
+            ss = row16_sum(ss);
+            *scale_out = norm ? inv_norm(ss) : 1.f;
+        };
 #pragma unroll
         for (int ps = 0; ps < KPASS; ++ps) {
             const int idx = tid + NT * ps, t = idx / kPPT, part = idx % kPPT;
             const bool live = t < nt;
-            float kk = 0.f, qq = 0.f;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const float x = live ? xk[ps][i] : 0.f;
-                sk[t][part + kPPT * i] = x;
-                kk = fmaf(x, x, kk);
-            }
-            if (want_o) {
-#pragma unroll
-                for (int i = 0; i < CPT; ++i) {
-                    const float y = live ? xq[ps][i] : 0.f;
-                    sq[t][part + kPPT * i] = y;
-                    qq = fmaf(y, y, qq);
-                }
-            }
-            kk = row16_sum(kk);
-            qq = row16_sum(qq);
+            float kn, qn = 1.f;
+            stage_row(xk[ps], live, norm_k, &sk[t][part], &kn);
+            if (want_o) stage_row(xq[ps], live, norm_q, &sq[t][part], &qn);
             if (part == 0 && live) {
-                skn[t] = norm_k ? inv_norm(kk) : 1.f;
-                sqn[t] = norm_q ? inv_norm(qq) : 1.f;
+                skn[t] = kn;
+                sqn[t] = qn;
             }
         }
 #pragma unroll

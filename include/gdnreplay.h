@@ -151,9 +151,10 @@ gdn_status gdn_tail_replay(const gdn_shape *shape,
  * kv_src should be pinned host memory (hipHostMalloc) for the copy to run
  * asynchronously; kv_dst is device memory of kv_bytes; copy_done is an event
  * created by the caller (the library creates and keeps none).  The streams
- * should be distinct for the two to overlap.  Errors: those of gdn_tail_replay
- * (nothing queued), GDN_ERR_INVALID_ARGUMENT for a NULL copy_done or a NULL
- * kv_dst / kv_src with kv_bytes > 0 (nothing queued), GDN_ERR_HIP when a
+ * should be distinct for the two to overlap.  Errors: those of gdn_tail_replay,
+ * GDN_ERR_INVALID_ARGUMENT for a NULL copy_done or a NULL kv_dst / kv_src with
+ * kv_bytes > 0; every argument of both the replay and the copy is checked
+ * before step 1, so none of these queues anything.  GDN_ERR_HIP when a
  * runtime call fails (earlier steps may have been queued).
  */
 typedef struct ihipEvent_t *hipEvent_t;

@@ -58,7 +58,6 @@ __all__ = [
     "tail_span",
     "resume_span",
     "prefill_span",
-    "run_pairs",
     "scan_rank1_c",
     "c_oracle_available",
     "rel_fro",
@@ -193,50 +192,6 @@ def resume_span(positions: Sequence[int], depth: int):
 def prefill_span(n_tokens: int):
     """(first position, length) of the full prefill 1..N."""
     return 1, int(n_tokens)
-
-
-# ---------------------------------------------------------------------------
-# packed-layout driver: q,k [rows][H][d_k], v [rows][H][d_v], alpha,beta [rows][H]
-# ---------------------------------------------------------------------------
-
-
-def run_pairs(pairs, q, k, v, alpha, beta, tok_offset, first_pos, spans, init_states,
-              *, normalize_k=True, normalize_q=False, emit=None, form="rank1"):
-    """Run the scan for selected (request, head) pairs of a packed batch.
-
-    pairs       iterable of (b, h)
-    q,k,v,...   float64-convertible arrays in the packed token-major layout
-    tok_offset  [B+1] rows of request b are tok_offset[b] .. tok_offset[b+1]-1
-    first_pos   [B] 1-based position held by row tok_offset[b]
-    spans       [B] (first position, length) to scan
-    init_states callable (b, h) -> (d_v, d_k) array (the start state)
-    emit        None or [B] list of token counts (relative to span start)
-    form        "rank1", "literal" or "c"
-    Returns {(b, h): (S_end, O_span, {t: S_t})}.
-    """
-    res = {}
-    for (b, h) in pairs:
-        p0, n = spans[b]
-        r0 = int(tok_offset[b]) + (int(p0) - int(first_pos[b]))
-        sl = slice(r0, r0 + int(n))
-        qq = np.asarray(q[sl, h], np.float64)
-        kk = np.asarray(k[sl, h], np.float64)
-        vv = np.asarray(v[sl, h], np.float64)
-        aa = np.asarray(alpha[sl, h], np.float64)
-        bb = np.asarray(beta[sl, h], np.float64)
-        e = () if emit is None else emit[b]
-        S0 = init_states(b, h)
-        if form == "literal":
-            r = scan_literal(S0, qq, kk, vv, aa, bb, normalize_k=normalize_k,
-                             normalize_q=normalize_q, emit_after=e)
-        elif form == "c":
-            r = scan_rank1_c(S0, qq, kk, vv, aa, bb, normalize_k=normalize_k,
-                             normalize_q=normalize_q, emit_after=e)
-        else:
-            r = scan_rank1(S0, qq, kk, vv, aa, bb, normalize_k=normalize_k,
-                           normalize_q=normalize_q, emit_after=e)
-        res[(b, h)] = r
-    return res
 
 
 def rel_fro(x, ref) -> float:

@@ -66,6 +66,36 @@ def oracle_pairs(w, pairs, *, tensors=None, init=None, emit=None, use_c=True):
     return res
 
 
+def _host(t):
+    return None if t is None else t.detach().cpu()
+
+
+def check_batched(w, outs, pairs=None, *, batch=64, tensors=None, init=None, emit=None, tol=None,
+                  label="", log=print):
+    """Compare one or more library results with the oracle on every pair of
+    ``pairs`` (default: all (request, head) pairs), running the C oracle on
+    ``batch`` pairs at a time so that full-size workloads fit in host memory.
+
+    outs: {name: (state_out, o or None, ckpt or None)} of device tensors.
+    Returns {name: worst errors}."""
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)] if pairs is None else list(pairs)
+    q, k, v, a, bt = tensors or (w.q, w.k, w.v, w.alpha, w.beta)
+    host = workloads.Workload(**{**w.__dict__, "q": _host(q), "k": _host(k), "v": _host(v),
+                                 "alpha": _host(a), "beta": _host(bt)})
+    h_outs = {n: tuple(_host(t) for t in ts) for n, ts in outs.items()}
+    worst = {n: {"state": 0.0, "o": 0.0, "emit": 0.0} for n in outs}
+    for i in range(0, len(pairs), batch):
+        sel = pairs[i:i + batch]
+        ref = oracle_pairs(host, sel, init=init, emit=emit)
+        for n, (S, O, C) in h_outs.items():
+            got = compare(host, ref, S, O, C, tol=tol, label=f"{label}[{n}]")
+            for key in got:
+                worst[n][key] = max(worst[n][key], got[key])
+        del ref
+    log(f"[{label}] {len(pairs)} pairs, worst rel err {worst}")
+    return worst
+
+
 def init_for(w):
     """Start state per pair for a resume workload (None: zero start)."""
     if w.op != "resume":

@@ -1,9 +1,9 @@
 """GPU parity: the HIP library against the fp64 oracle, through the C ABI.
 
-Small cases are checked on every (request, head) pair; the headline workloads
-run at full size in the launch configuration the benchmark uses and are
-checked on sampled pairs.  Rows outside every span are NaN-poisoned, so any
-read outside a span shows up as a NaN in the results.
+Every case, the headline workloads at full size in the launch configuration
+the benchmark uses included, is checked on every (request, head) pair (the C
+oracle runs a batch of pairs at a time).  Rows outside every span are
+NaN-poisoned, so any read outside a span shows up as a NaN in the results.
 """
 import os
 
@@ -148,7 +148,7 @@ def test_random_small_cases(gdn, kernel):
         _check_workload(gdn, w, kernel, label=f"random-{i}")
 
 
-# --- the headline workloads at full size, sampled pairs ------------------------
+# --- the headline workloads at full size, every pair ------------------------------
 
 def _sample_pairs(w, n, seed):
     rng = np.random.default_rng(seed)
@@ -162,37 +162,60 @@ def _sample_pairs(w, n, seed):
     return pairs
 
 
-FULL_SIZE = {"resume_B8_H16_N8192": (24, 2), "tail5_B16_H32_m32768": (24, 3), "prefill_emit_B4_H32_N65536": (4, 5)}
+FULL_SIZE = ["resume_B8_H16_N8192", "tail5_B16_H32_m32768", "prefill_emit_B4_H32_N65536"]
 
 
-@pytest.mark.parametrize("name", list(FULL_SIZE))
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_full_size_workloads(gdn, name):
+    """The resume (8 x 16 pairs, N = 8192), 5% tail replay (16 x 32 pairs,
+    k = 1639) and prefill with emission (4 x 32 pairs, N = 65536, 16 emissions)
+    workloads at full size, in the benchmark's launch configuration, against
+    the oracle on all of their (request, head) pairs.  The prefill also runs
+    through the three-segment split path, held to the same bar."""
     w = W.named(name, device="cuda")
-    npairs, seed = FULL_SIZE[name]
-    _check_workload(gdn, w, "auto", pairs=_sample_pairs(w, npairs, seed), poison=name.startswith("resume"),
-                    label=name)
+    spans = PT.spans_of(w)
+    if name.startswith("resume"):
+        W.poison_outside(w, spans)
+    _log(f"[{name}] full size, all {w.B * w.H} pairs")
+    res = PT.run_library(gdn, w)
+    outs = {"one pass": (res["state"], res["o"], res.get("ckpt"))}
+    if w.op == "prefill":
+        C, S, O = gdn.prefill_emit_checkpoints_split(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset,
+                                                     w.ckpt_pos, flags=w.flags)
+        outs["three segments"] = (S, O, C)
+    torch.cuda.synchronize()
+    if w.op == "tail":
+        assert res["k"] == [oracle.tail_length(m, w.r_num, w.r_den) for m in w.m]
+    if w.op == "resume":
+        assert res["j"] == [oracle.select_checkpoint(w.ckpt_pos[b], w.depth[b]) for b in range(w.B)]
+    PT.check_batched(w, outs, init=PT.init_for(w), emit=PT.emit_for(w), batch=16 if w.op == "prefill" else 64,
+                     label=name, log=_log)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_full_size_tail_on_the_per_token_kernel(gdn, dtype):
     """The 5% tail replay at full size (16 x 32 pairs, m = 32768, k = 1639) forced
     onto the exact per-token kernel, with bf16 inputs (bar 3e-3) and float32
-    inputs (bar 1e-5), on sampled pairs."""
+    inputs (bar 1e-5), on every pair."""
     w = W.tail(device="cuda", dtype=dtype, name=f"tail5_B16_H32_m32768_{dtype}")
-    _check_workload(gdn, w, "recurrent", pairs=_sample_pairs(w, 16, 11), poison=False,
-                    label=f"tail5 per-token {dtype}")
+    res = PT.run_library(gdn, w, flags_extra=KERNELS["recurrent"])
+    torch.cuda.synchronize()
+    PT.check_batched(w, {"per-token": (res["state"], res["o"], None)}, label=f"tail5 per-token {dtype}",
+                     log=_log)
 
 
 def test_grouped_tail_three_layers(gdn):
     """Three linear-attention layers replayed in sequence, each layer's bf16
-    outputs being the next layer's q = k = v (identity mixing).  Per layer, the
-    library runs on the oracle's own bf16-rounded outputs of the previous layer
-    (teacher forcing), so each layer is held to the bf16 bar.  The free-running
-    GPU chain is also compared end to end as a diagnostic: after layer 1 the two
-    chains read different bf16 inputs (rounding decisions on o differ), so that
-    difference compounds and is only held to a loose 1e-2 bound."""
+    outputs being the next layer's q = k = v (identity mixing), on all 512
+    (request, head) pairs.  Per layer, the library runs on the oracle's own
+    bf16-rounded outputs of the previous layer (teacher forcing), so each layer
+    is held to the bf16 bar.  The free-running GPU chain (each layer fed the
+    GPU's own previous outputs) is compared with the oracle's free-running
+    chain (its own bf16 rounding between layers) and held to the same bar:
+    this is the error propagation across the layers of a group that the
+    grouped workload exists to exercise."""
     w = W.named("tail10_grouped_B16_H32_m32768_L3", device="cuda")
-    pairs = _sample_pairs(w, 8, 4)
+    pairs = _all_pairs(w)
     spans = PT.spans_of(w)
     alphas = [w.alpha] + list(w.layer_alpha)
     betas = [w.beta] + list(w.layer_beta)
@@ -213,8 +236,14 @@ def test_grouped_tail_three_layers(gdn):
                            "beta": betas[layer]})
         res = PT.run_library(gdn, wl)
         torch.cuda.synchronize()
-        ref = PT.oracle_pairs(wl, pairs)
-        worst = PT.compare(wl, ref, res["state"], res["o"], label=f"grouped-L{layer + 1}")
+        ref = {}
+        worst = {"state": 0.0, "o": 0.0, "emit": 0.0}
+        for i in range(0, len(pairs), 64):
+            part = PT.oracle_pairs(wl, pairs[i:i + 64])
+            got = PT.compare(wl, part, res["state"], res["o"], label=f"grouped-L{layer + 1}")
+            worst = {key: max(worst[key], got[key]) for key in worst}
+            # keep only what the next layer's teacher-forced input needs
+            ref.update({p: (None, O, None, sl) for p, (S, O, st, sl) in part.items()})
         _log(f"[grouped] layer {layer + 1} teacher-forced worst {worst}")
         ref_prev = ref
         # free-running chain on the GPU
@@ -232,19 +261,31 @@ def test_grouped_tail_three_layers(gdn):
     fk = bool(w.flags & W.NORMALIZE_K)
     fq = bool(w.flags & W.NORMALIZE_Q)
     worst_chain = 0.0
-    for (b, h) in pairs:
-        (qq, kk, vv, aa, bb), sl = PT.pair_inputs(w, b, h, spans[b])
+    free_state = free_state.cpu()
+    host_in = [t.cpu() for t in (q, k, v)]
+    host_a = [t.cpu() for t in alphas]
+    host_b = [t.cpu() for t in betas]
+    for i in range(0, len(pairs), 64):
+        sel = pairs[i:i + 64]
+        xs = []
+        for (b, h) in sel:
+            (qq, kk, vv, _, _), sl = PT.pair_inputs(w, b, h, spans[b], tensors=(*host_in, host_a[0], host_b[0]))
+            xs.append((qq, kk, vv, sl))
         for layer in range(3):
-            a_l = PT.np64(alphas[layer][sl, h])
-            b_l = PT.np64(betas[layer][sl, h])
-            S, O, _ = oracle.scan_rank1_c(np.zeros((w.dv, w.dk)), qq, kk, vv, a_l, b_l,
-                                          normalize_k=fk, normalize_q=fq)
-            Ob = PT.np64(torch.from_numpy(O).to(torch.bfloat16))
-            qq = kk = vv = Ob
-        e = oracle.rel_fro(PT.np64(free_state[b, h]), S)
-        worst_chain = max(worst_chain, e)
-    _log(f"[grouped] free-running 3-layer chain worst state rel err {worst_chain:.3g}")
-    assert worst_chain <= 1e-2
+            S, O, _ = oracle.scan_rank1_c_batch(
+                [np.zeros((w.dv, w.dk))] * len(sel), [x[0] for x in xs], [x[1] for x in xs],
+                [x[2] for x in xs], [PT.np64(host_a[layer][x[3], h]) for x, (b, h) in zip(xs, sel)],
+                [PT.np64(host_b[layer][x[3], h]) for x, (b, h) in zip(xs, sel)], normalize_k=fk, normalize_q=fq)
+            nxt = []
+            for j, x in enumerate(xs):
+                Ob = PT.np64(torch.from_numpy(O[j]).to(torch.bfloat16))
+                nxt.append((Ob, Ob, Ob, x[3]))
+            xs = nxt
+        for j, (b, h) in enumerate(sel):
+            e = oracle.rel_fro(PT.np64(free_state[b, h]), S[j])
+            worst_chain = max(worst_chain, e)
+            assert e <= PT.TOL["bf16"], f"free-running chain (b={b}, h={h}): rel err {e:.3g} > 3e-3"
+    _log(f"[grouped] free-running 3-layer chain worst state rel err {worst_chain:.3g} over {len(pairs)} pairs")
 
 
 # --- edge cases ----------------------------------------------------------------
@@ -405,7 +446,8 @@ def test_planned_checkpoints_drive_prefill_and_resume(gdn):
 @pytest.mark.parametrize("kernel", ["recurrent", "auto"])
 def test_tail_replay_with_h2d_matches_plain(gdn, kernel):
     """The overlapped entry point ([TR] §2.5) gives the plain replay's results
-    bit for bit, and the transfer lands intact before later work on the stream."""
+    bit for bit, those results match the oracle, and the transfer lands intact
+    before later work on the stream."""
     w = W.tail(seed=41, B=3, H=4, d=128, m=2000, m_list=[2000, 777, 1500])
     PT.to_device(w)
     flags = w.flags | KERNELS[kernel]
@@ -420,14 +462,16 @@ def test_tail_replay_with_h2d_matches_plain(gdn, kernel):
                                           w.r_den, src, dst, cs, ev, first_pos=w.first_pos, flags=flags)
     chk = dst.sum(dtype=torch.int64)  # queued on the current stream, after the join
     torch.cuda.synchronize()
-    assert k1 == k0
+    assert k1 == k0 == [oracle.tail_length(m, w.r_num, w.r_den) for m in w.m]
     assert torch.equal(S1, S0) and torch.equal(O1, O0)
     assert int(chk) == int(src.sum(dtype=torch.int64)) and torch.equal(dst.cpu(), src)
+    # and the overlapped call's own results against the oracle, on every pair
+    PT.check_batched(w, {"overlapped": (S1, O1, None)}, label=f"h2d-{kernel}", log=_log)
 
 
 def test_tail_replay_with_h2d_overlaps(gdn):
     """[TR] §2.5 latency model: with the KV transfer on its own stream the two
-    take about max(T_KV, T_replay), less than the serial sum."""
+    take about max(T_KV, T_replay) (logged), less than the serial sum (asserted)."""
     w = W.named("tail5_B16_H32_m32768", device="cuda")
     st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
     o = torch.empty_like(w.v)
@@ -462,9 +506,10 @@ def test_tail_replay_with_h2d_overlaps(gdn):
     t_ov = timed(lambda: gdn.tail_replay_with_h2d(w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m,
                                                   w.r_num, w.r_den, src, dst, cs, ev, first_pos=w.first_pos,
                                                   flags=w.flags, state_out=st, o=o))
-    _log(f"[overlap] T_replay={t_rep:.3f} T_KV={t_kv:.3f} serial={t_ser:.3f} overlapped={t_ov:.3f} ms")
+    _log(f"[overlap] T_replay={t_rep:.3f} T_KV={t_kv:.3f} serial={t_ser:.3f} overlapped={t_ov:.3f} ms; "
+         f"overlapped / max(T_KV, T_replay) = {t_ov / max(t_kv, t_rep):.3f}")
+    # only the ordering is asserted: the ratio to the model depends on the box's clock
     assert t_ov < t_ser
-    assert t_ov <= 1.15 * max(t_kv, t_rep) + 0.05
 
 
 @pytest.mark.parametrize("alpha_rng", [(0.98, 0.99), (0.95, 1.0)])
@@ -542,11 +587,11 @@ def test_split_prefill_parity(gdn, dtype, d):
     _split_check(gdn, w, f"split-{dtype}-{d}")
 
 
-def test_split_prefill_full_size(gdn):
-    """The prefill workload (4 x 32 pairs, N = 65536, 16 emissions) through the
-    split path, on sampled pairs, and its time next to the one-pass prefill."""
+def test_split_prefill_full_size_time(gdn):
+    """The prefill workload (4 x 32 pairs, N = 65536, 16 emissions): time of the
+    split path next to the one-pass prefill (its parity on every pair is part
+    of test_full_size_workloads)."""
     w = W.named("prefill_emit_B4_H32_N65536", device="cuda")
-    _split_check(gdn, w, "prefill64k-split", pairs=_sample_pairs(w, 4, 5))
     ws = torch.empty(gdn.prefill_split_workspace_bytes(w.B, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
     st = torch.empty(w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
     ck = torch.empty(w.B, len(w.ckpt_pos[0]), w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
@@ -883,3 +928,62 @@ def test_runs_are_deterministic(gdn, B, flags):
     for S, O in outs[1:]:
         assert torch.equal(S.view(torch.int32), outs[0][0].view(torch.int32))
         assert torch.equal(O.view(torch.int16), outs[0][1].view(torch.int16))
+
+
+# --- accuracy over the domain of the contraction condition ----------------------------
+# [TR] §2.3 states its error bound for unit keys, beta in [0, 2] and alpha <= rho.
+# The chunked kernel's fp16 operands and its compact-WY solve are exercised here
+# on the inputs where they are weakest: keys clustered near a few directions (a
+# nearly rank-deficient Gram matrix per chunk) with beta up to 2, long runs
+# without decay (alpha = 1), zero keys and keys far from unit norm.
+
+def _domain_tail(seed, k_len=2048, B=2, H=8, alpha_rng=(0.95, 1.0), beta_hi=2.0):
+    m = k_len * 20  # r = 5% of m is exactly k_len tokens
+    return W.tail(seed=seed, B=B, H=H, d=128, m=m, r_num=5, r_den=100, alpha_rng=alpha_rng,
+                  beta_hi=beta_hi, name=f"tail_k{k_len}_beta{beta_hi}")
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+@pytest.mark.parametrize("op", ["tail", "prefill"])
+def test_clustered_keys_beta_up_to_two(gdn, kernel, op):
+    """Keys within 0.15 of four directions per head (in-cluster cosines about
+    0.98), beta ~ U(0, 2), alpha ~ U[0.95, 1], 2048-token spans (prefill: with
+    four emissions), every pair against the oracle."""
+    if op == "tail":
+        w = _domain_tail(seed=201)
+    else:
+        w = W.prefill(seed=202, B=2, H=8, d=128, N=2048, M=4, alpha_rng=(0.95, 1.0), beta_hi=2.0)
+    W.cluster_keys(w, n_dirs=4, spread=0.15, seed=201)
+    _check_workload(gdn, w, kernel, label=f"clustered-{op}")
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+@pytest.mark.parametrize("keys", ["random", "clustered"])
+@pytest.mark.parametrize("beta_hi", [1.0, 2.0])
+def test_alpha_one_long_spans(gdn, kernel, keys, beta_hi):
+    """alpha = 1 on every token of 2048-token spans (no decay at all: the case
+    where [TR] §2.3's bound gives nothing), with beta ~ U(0, 1) or U(0, 2) and
+    random or clustered unit keys, every pair against the oracle."""
+    w = _domain_tail(seed=211 + int(beta_hi), alpha_rng=(1.0, 1.0), beta_hi=beta_hi)
+    assert bool((w.alpha == 1).all())
+    if keys == "clustered":
+        W.cluster_keys(w, n_dirs=4, spread=0.15, seed=212)
+    _check_workload(gdn, w, kernel, label=f"alpha1-{keys}-beta{beta_hi}")
+
+
+@pytest.mark.parametrize("kernel", ["recurrent", "auto"])
+@pytest.mark.parametrize("op", ["tail", "resume", "prefill"])
+def test_key_norms_zero_and_extreme(gdn, kernel, op):
+    """Keys and queries (both normalised by the kernel) with row norms from
+    1e-3 to 1e3, every seventh key zero (it must stay zero: no epsilon in the
+    norm), and single rows at 1e-20 and 1e20, whose float32 sums of squares
+    would underflow or overflow if formed directly; every pair against the
+    oracle, which normalises in float64."""
+    w = _small(op, "bf16", 128, 128, seed=221)
+    spans = PT.spans_of(w)
+    rows = [w.tok_offset[b] + (p0 - w.first_pos[b]) for b, (p0, n) in enumerate(spans) if n > 8]
+    ext_k = [(rows[0] + 3, 1e-20), (rows[0] + 5, 1e20), (rows[-1] + 1, 1e20), (rows[-1] + 2, 1e-20)]
+    W.scale_rows(w, "k", zero_every=7, extreme=ext_k, seed=221)
+    W.scale_rows(w, "q", extreme=[(rows[0] + 4, 1e20), (rows[-1] + 3, 1e-20)], seed=222)
+    assert float(w.k.float().abs().max()) > 1e18 and int((w.k.float().abs().amax(-1) == 0).sum()) > 0
+    _check_workload(gdn, w, kernel, label=f"key-norms-{op}")

@@ -202,3 +202,31 @@ def test_overlapped_replay_argument_errors(gdn):
     assert call(FAKE, None, 1024, FAKE) == 1
     # replay arguments are validated first: nothing is queued on an invalid ratio
     assert call(FAKE, FAKE, 1024, FAKE, r_den=0) == 1 and "ratio" in lib.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("case", ["misaligned q, chunked required", "NULL k", "o without q",
+                                  "state_out misaligned"])
+def test_overlapped_replay_checks_the_replay_before_the_copy(gdn, case):
+    """Every argument of the replay (pointers, alignment, kernel choice) is
+    checked before the copy is queued: with placeholder copy arguments, a
+    queued copy would fail in the runtime (GDN_ERR_HIP, no GPU here), so the
+    replay's own error code shows that nothing was queued."""
+    lib = gdn.load()
+    flags = 1 | (512 if case.startswith("misaligned q") else 0)
+    sh = gdn._Shape(B=2, H=2, dk=128, dv=128, dtype=1, flags=flags)
+    off = gdn._i64([0, 10, 20])
+    m = gdn._i64([10, 10])
+    p = ctypes.c_void_p(FAKE)
+    q, k, state, o = p, p, p, p
+    if case.startswith("misaligned q"):
+        q = ctypes.c_void_p(FAKE + 2)
+    elif case == "NULL k":
+        k = None
+    elif case == "o without q":
+        q = None
+    else:
+        state = ctypes.c_void_p(FAKE + 4)
+    st = lib.gdn_tail_replay_with_h2d(ctypes.byref(sh), q, k, p, p, p, gdn._p64(off), None, gdn._p64(m),
+                                      5, 100, state, o, None, p, p, 1 << 20, None, None, p)
+    want = 2 if case.startswith("misaligned q") else 1
+    assert st == want, (st, lib.gdn_last_error().decode())

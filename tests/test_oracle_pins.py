@@ -399,3 +399,66 @@ def test_c_oracle_rejects_bad_emission_lists():
     with pytest.raises(ValueError):
         oracle.scan_rank1_c_batch([S[0]], [k], [k], [k], [np.ones(3)], [np.ones(3)],
                                   emits=[[4]])
+
+
+# --- the parity metric -------------------------------------------------------------
+
+def _rel_fro_pins(rel_fro):
+    """Known answers of ||x - ref||_F / ||ref||_F, the relative Frobenius error
+    every parity verdict is stated in (per (request, head) slice)."""
+    ref = np.array([[3.0, 4.0]])
+    # x = ref (1 + eps): the error is |eps|, whatever the sign of eps
+    for eps in (1e-3, -2.5e-6, 0.5):
+        assert rel_fro(ref * (1 + eps), ref) == pytest.approx(abs(eps), rel=1e-12)
+    # the denominator is the reference's norm, not the result's: x = 2 ref gives 1, ref = 2 x gives 1/2
+    assert rel_fro(2 * ref, ref) == pytest.approx(1.0, rel=1e-15)
+    assert rel_fro(ref, 2 * ref) == pytest.approx(0.5, rel=1e-15)
+    # a sign flip is an error of 2; a zero result an error of 1
+    assert rel_fro(-ref, ref) == pytest.approx(2.0, rel=1e-15)
+    assert rel_fro(np.zeros_like(ref), ref) == pytest.approx(1.0, rel=1e-15)
+    # Frobenius over every entry of a matrix: one entry of the 3 x 3 identity off by 1 -> 1/sqrt(3)
+    x = np.eye(3)
+    x[2, 0] = 1.0
+    assert rel_fro(x, np.eye(3)) == pytest.approx(1 / np.sqrt(3), rel=1e-15)
+    # a zero reference demands an exact zero: 0 -> 0, anything else -> inf
+    assert rel_fro(np.zeros((2, 2)), np.zeros((2, 2))) == 0.0
+    assert rel_fro(np.array([[0.0, 1.4e-45]]), np.zeros((1, 2))) == np.inf  # the smallest float32 denormal
+    # empty slices (a zero-length span) compare as equal
+    assert rel_fro(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+
+
+def test_rel_fro_known_answers():
+    _rel_fro_pins(oracle.rel_fro)
+
+
+def _rel_fro_mutants():
+    fro = lambda a: float(np.sqrt(np.sum(np.asarray(a, np.float64) ** 2)))
+
+    def by_result(x, ref):  # divides by ||x|| instead of ||ref||
+        d = fro(x)
+        return fro(np.asarray(x) - ref) / d if d else (0.0 if fro(np.asarray(x) - ref) == 0 else np.inf)
+
+    def zero_ref_passes(x, ref):  # ||ref|| = 0 reported as 0 whatever x is
+        d = fro(ref)
+        return fro(np.asarray(x) - ref) / d if d else 0.0
+
+    def max_abs(x, ref):  # largest entry instead of the Frobenius norm
+        d = float(np.max(np.abs(ref))) if np.size(ref) else 0.0
+        n = float(np.max(np.abs(np.asarray(x) - ref))) if np.size(ref) else 0.0
+        return n / d if d else (0.0 if n == 0 else np.inf)
+
+    def squared(x, ref):  # ratio of squared norms
+        d = fro(ref) ** 2
+        n = fro(np.asarray(x) - ref) ** 2
+        return n / d if d else (0.0 if n == 0 else np.inf)
+
+    return {"divides by the result's norm": by_result, "zero reference always passes": zero_ref_passes,
+            "max-abs instead of Frobenius": max_abs, "squared ratio": squared}
+
+
+@pytest.mark.parametrize("name", list(_rel_fro_mutants()))
+def test_rel_fro_mutants_fail_the_pins(name):
+    """Planted mistakes in the metric (in this test, never in the oracle) each
+    fail one of the known answers above."""
+    with pytest.raises(AssertionError):
+        _rel_fro_pins(_rel_fro_mutants()[name])

@@ -194,6 +194,40 @@ def tail(device="cpu", seed=3, B=16, H=32, d=128, m=32768, r_num=5, r_den=100,
                     layer_beta=lb or None, seed=seed)
 
 
+def cluster_keys(w: Workload, n_dirs: int = 4, spread: float = 0.15, seed: int = 0) -> Workload:
+    """Replace the keys by unit keys clustered near ``n_dirs`` random directions
+    per head: key = (c_j + spread * z) / ||c_j + spread * z|| with a random
+    cluster j per token, c_j unit and z ~ N(0, I / d_k).  Inside a cluster the
+    cosine between two keys is about 1 / (1 + spread^2), i.e. the Gram matrix
+    of a chunk's keys is close to rank n_dirs."""
+    g = torch.Generator().manual_seed(10_000 + seed)
+    rows, H, dk = w.k.shape
+    centres = _unit_rows(torch.randn(H, n_dirs, dk, generator=g, dtype=torch.float64))
+    pick = torch.randint(0, n_dirs, (rows, H), generator=g)
+    z = torch.randn(rows, H, dk, generator=g, dtype=torch.float64) / dk ** 0.5
+    k = _unit_rows(centres[torch.arange(H)[None, :], pick] + spread * z)
+    w.k = k.to(dtype=w.k.dtype, device=w.k.device)
+    return w
+
+
+def scale_rows(w: Workload, which: str = "k", log10_range=(-3.0, 3.0), zero_every: int = 0,
+               extreme=(), seed: int = 0) -> Workload:
+    """Multiply each row of q or k by 10^u, u ~ U(log10_range), set every
+    ``zero_every``-th row (if > 0) to zero, and give the rows listed in
+    ``extreme`` as (row, factor) that exact factor instead (e.g. 1e-20, 1e20)."""
+    g = torch.Generator().manual_seed(20_000 + seed)
+    t = getattr(w, which)
+    rows, H, _ = t.shape
+    f = torch.pow(10.0, torch.empty(rows, H, 1, dtype=torch.float64).uniform_(*log10_range, generator=g))
+    if zero_every > 0:
+        f[::zero_every] = 0.0
+    for r, fac in extreme:
+        f[r] = fac
+    x = t.to(device="cpu", dtype=torch.float64) * f
+    setattr(w, which, x.to(dtype=t.dtype, device=t.device))
+    return w
+
+
 def poison_outside(w: Workload, spans) -> None:
     """Fill every row that lies outside spans[b] = (first position, length) with NaN."""
     keep = torch.zeros(w.rows, dtype=torch.bool)
