@@ -24,7 +24,8 @@ __all__ = [
     "GDNError", "NORMALIZE_K", "NORMALIZE_Q", "KERNEL_RECURRENT", "KERNEL_CHUNKED",
     "MAX_CHECKPOINTS", "library_path", "load", "version", "kernel_for", "tail_len", "select_checkpoint",
     "tail_replay", "tail_replay_with_h2d", "resume", "prefill_emit_checkpoints",
-    "prefill_split_workspace_bytes", "prefill_emit_checkpoints_split",
+    "prefill_split_workspace_bytes", "prefill_emit_checkpoints_split", "SPLIT_SCRATCH_BYTES",
+    "prefill_emit_checkpoints_split_noalloc",
     "expected_recompute", "balanced_checkpoints", "plan_checkpoints",
 ]
 
@@ -33,6 +34,7 @@ NORMALIZE_Q = 2
 KERNEL_RECURRENT = 256
 KERNEL_CHUNKED = 512
 MAX_CHECKPOINTS = 192
+SPLIT_SCRATCH_BYTES = 32 << 20  # GDN_SPLIT_SCRATCH_BYTES
 
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARGUMENT", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_HIP"}
@@ -95,6 +97,9 @@ def load():
     lib.gdn_prefill_emit_checkpoints_split.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p,
                                                        ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gdn_prefill_emit_checkpoints_split.restype = ctypes.c_int
+    lib.gdn_prefill_emit_checkpoints_split_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p,
+                                                               ctypes.c_int32, vp, vp, vp, vp]
+    lib.gdn_prefill_emit_checkpoints_split_noalloc.restype = ctypes.c_int
     f64p = ctypes.POINTER(ctypes.c_double)
     lib.gdn_expected_recompute.argtypes = [f64p, ctypes.c_int64, i64p, ctypes.c_int32]
     lib.gdn_expected_recompute.restype = ctypes.c_double
@@ -372,4 +377,30 @@ def prefill_emit_checkpoints_split(q, k, v, alpha, beta, tok_offset, ckpt_pos, *
         _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
         _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(k.device)))
+    return ckpt_states, state_out, o
+
+
+def prefill_emit_checkpoints_split_noalloc(q, k, v, alpha, beta, tok_offset, ckpt_pos, *, flags=NORMALIZE_K,
+                                           ckpt_states=None, state_out=None, o=None, want_o=True):
+    """prefill_emit_checkpoints_split with its workspace in the library's fixed
+    per-GPU scratch (SPLIT_SCRATCH_BYTES): the library allocates nothing.  The
+    caller passes (or this wrapper allocates) only the outputs.  Calls that
+    overlap on one GPU share that scratch and must be ordered (one stream).
+
+    Returns (ckpt_states [B,M,H,d_v,d_k], state_out [B,H,d_v,d_k], o or None)."""
+    if want_o and o is None:
+        o = torch.empty_like(v)
+    rows, H, dk, dv, dt = _check_tensors(q if o is not None else None, k, v, alpha, beta, o)
+    off = _i64(tok_offset)
+    B = int(off.size) - 1
+    off, _ = _rows_meta(off, None, rows, B)
+    pos = np.ascontiguousarray(np.asarray(ckpt_pos, dtype=np.int64).reshape(B, -1))
+    M = int(pos.shape[1])
+    ckpt_states = _state(ckpt_states, (B, M, H, dv, dk), k.device, "ckpt_states")
+    state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
+    sh = _shape(B, H, dk, dv, dt, flags)
+    _check(load().gdn_prefill_emit_checkpoints_split_noalloc(
+        ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
+        _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o), _stream(k.device)))
     return ckpt_states, state_out, o

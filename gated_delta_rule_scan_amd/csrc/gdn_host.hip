@@ -23,6 +23,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -530,16 +531,14 @@ GDN_API size_t gdn_prefill_split_workspace_bytes(const gdn_shape *shape) {
     return (size_t)4 * shape->B * shape->H * shape->dv * shape->dk * sizeof(float);
 }
 
-GDN_API gdn_status gdn_prefill_emit_checkpoints_split(const gdn_shape *shape, const void *q,
-                                                      const void *k, const void *v,
-                                                      const void *alpha, const void *beta,
-                                                      const int64_t *h_tok_offset,
-                                                      const int64_t *h_first_pos,
-                                                      const int64_t *h_ckpt_pos, int32_t M,
-                                                      float *ckpt_states, float *state_out, void *o,
-                                                      void *workspace, size_t workspace_bytes,
-                                                      hipStream_t stream) {
-    g_last_error.clear();
+namespace {
+
+// The split prefill on a caller's workspace (workspace_bytes long).
+gdn_status split_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                         const void *alpha, const void *beta, const int64_t *h_tok_offset,
+                         const int64_t *h_first_pos, const int64_t *h_ckpt_pos, int32_t M,
+                         float *ckpt_states, float *state_out, void *o, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
     std::vector<Work> whole;
     gdn_status st = prepare_prefill(shape, h_tok_offset, h_first_pos, h_ckpt_pos, M, ckpt_states, state_out, whole);
     if (st != GDN_OK || shape->B == 0) return st;
@@ -613,4 +612,79 @@ GDN_API gdn_status gdn_prefill_emit_checkpoints_split(const gdn_shape *shape, co
                                                     stream);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
     return run(shape, q, k, v, alpha, beta, o, ws, ckpt_states, M, second, stream);
+}
+
+// Fixed scratch of the allocation-free split prefill: one array per GPU, in the
+// library's code object (held until the process ends).  In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address is
+// taken per device with hipGetSymbolAddress and only that address is used.
+__device__ __align__(256) float scratch[GDN_SPLIT_SCRATCH_BYTES / sizeof(float)];
+
+std::mutex g_scratch_mu;
+std::vector<float *> g_scratch_ptr;  // device address of `scratch`, per device (NULL: not taken yet)
+
+// Device address of this device's scratch array, taken once per device with the
+// device current.
+gdn_status scratch_for_current_device(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch_ptr[(size_t)dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[(size_t)dev] = static_cast<float *>(ptr);
+    }
+    *out = g_scratch_ptr[(size_t)dev];
+    return GDN_OK;
+}
+
+}  // namespace
+
+GDN_API gdn_status gdn_prefill_emit_checkpoints_split(const gdn_shape *shape, const void *q,
+                                                      const void *k, const void *v,
+                                                      const void *alpha, const void *beta,
+                                                      const int64_t *h_tok_offset,
+                                                      const int64_t *h_first_pos,
+                                                      const int64_t *h_ckpt_pos, int32_t M,
+                                                      float *ckpt_states, float *state_out, void *o,
+                                                      void *workspace, size_t workspace_bytes,
+                                                      hipStream_t stream) {
+    g_last_error.clear();
+    return split_prefill(shape, q, k, v, alpha, beta, h_tok_offset, h_first_pos, h_ckpt_pos, M, ckpt_states,
+                         state_out, o, workspace, workspace_bytes, stream);
+}
+
+GDN_API gdn_status gdn_prefill_emit_checkpoints_split_noalloc(const gdn_shape *shape, const void *q,
+                                                              const void *k, const void *v,
+                                                              const void *alpha, const void *beta,
+                                                              const int64_t *h_tok_offset,
+                                                              const int64_t *h_first_pos,
+                                                              const int64_t *h_ckpt_pos, int32_t M,
+                                                              float *ckpt_states, float *state_out, void *o,
+                                                              hipStream_t stream) {
+    g_last_error.clear();
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK) return st;
+    const size_t need = gdn_prefill_split_workspace_bytes(shape);
+    if (need > (size_t)GDN_SPLIT_SCRATCH_BYTES)
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "the allocation-free split prefill needs %zu bytes of scratch (4 B H d_v d_k floats), more than "
+                    "its fixed %zu; use gdn_prefill_emit_checkpoints_split with a workspace",
+                    need, (size_t)GDN_SPLIT_SCRATCH_BYTES);
+    if (shape->B == 0) return GDN_OK;
+    // everything the host can check is checked before the scratch address is taken
+    std::vector<Work> probe;
+    if ((st = prepare_prefill(shape, h_tok_offset, h_first_pos, h_ckpt_pos, M, ckpt_states, state_out, probe)) !=
+        GDN_OK)
+        return st;
+    if (shape->dk != shape->dv)
+        return fail(GDN_ERR_UNSUPPORTED, "the split prefill needs d_k = d_v (got %d, %d)", shape->dk, shape->dv);
+    float *ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != GDN_OK) return st;
+    return split_prefill(shape, q, k, v, alpha, beta, h_tok_offset, h_first_pos, h_ckpt_pos, M, ckpt_states,
+                         state_out, o, ws, (size_t)GDN_SPLIT_SCRATCH_BYTES, stream);
 }

@@ -247,6 +247,40 @@ gdn_status gdn_prefill_emit_checkpoints_split(const gdn_shape *shape,
                                               void *workspace, size_t workspace_bytes,
                                               hipStream_t stream);
 
+/* Scratch bytes behind gdn_prefill_emit_checkpoints_split_noalloc, per GPU. */
+#define GDN_SPLIT_SCRATCH_BYTES (32u << 20)
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * split prefill as gdn_prefill_emit_checkpoints_split (same arguments except
+ * the workspace, same kernels, same results bit for bit), with its workspace
+ * taken from a fixed array of GDN_SPLIT_SCRATCH_BYTES (32 MiB) in the
+ * library's code object instead of from the caller.
+ *  - Limit: gdn_prefill_split_workspace_bytes(shape) = 4 B H d_v d_k floats
+ *    must not exceed GDN_SPLIT_SCRATCH_BYTES (B H <= 128 at d_k = d_v = 128),
+ *    else GDN_ERR_UNSUPPORTED and nothing is queued.
+ *  - Each GPU the library runs on holds its own copy of the array until the
+ *    process ends; the first call on a device looks up its address
+ *    (hipGetSymbolAddress, no allocation).  Nothing here calls hipMalloc,
+ *    hipFree or an allocating routine.
+ *  - Every call on a GPU shares that GPU's array and leaves its contents
+ *    behind; nothing in it has to start at zero (every value read was written
+ *    earlier in the same call).  Calls that overlap on one GPU (other streams,
+ *    other threads) race on the array: the caller must order them, e.g. on
+ *    one stream.
+ * Errors: those of gdn_prefill_emit_checkpoints_split (except the workspace
+ * ones); GDN_ERR_HIP if the array's address cannot be taken.
+ */
+gdn_status gdn_prefill_emit_checkpoints_split_noalloc(const gdn_shape *shape,
+                                                      const void *q, const void *k, const void *v,
+                                                      const void *alpha, const void *beta,
+                                                      const int64_t *h_tok_offset,
+                                                      const int64_t *h_first_pos,
+                                                      const int64_t *h_ckpt_pos, int32_t M,
+                                                      float *ckpt_states, float *state_out, void *o,
+                                                      hipStream_t stream);
+
 /*
  * Checkpoint placement ([SPC] §3 problem statement, §4 Theorems 1 and 2).
  * Host only, double precision, no device work.  A depth distribution p is an

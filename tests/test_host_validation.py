@@ -230,3 +230,34 @@ def test_overlapped_replay_checks_the_replay_before_the_copy(gdn, case):
                                       5, 100, state, o, None, p, p, 1 << 20, None, None, p)
     want = 2 if case.startswith("misaligned q") else 1
     assert st == want, (st, lib.gdn_last_error().decode())
+
+
+def test_noalloc_split_prefill_rejects_sizes_beyond_its_scratch(gdn):
+    """The allocation-free split prefill refuses a shape whose workspace
+    (4 B H d_v d_k floats) exceeds its fixed scratch, before any HIP call."""
+    lib = gdn.load()
+    assert gdn.SPLIT_SCRATCH_BYTES == 32 << 20
+    p = ctypes.c_void_p(FAKE)
+    ck, st = ctypes.c_void_p(1 << 36), ctypes.c_void_p(1 << 40)  # disjoint placeholder outputs
+    n = 1000
+
+    def call(B, H, d, M=1):
+        sh = gdn._Shape(B=B, H=H, dk=d, dv=d, dtype=1, flags=1)
+        off = gdn._i64([n * b for b in range(B + 1)])
+        pos = gdn._i64([n] * (B * M))
+        return lib.gdn_prefill_emit_checkpoints_split_noalloc(ctypes.byref(sh), p, p, p, p, p, gdn._p64(off),
+                                                              None, gdn._p64(pos), M, ck, st, p, None)
+
+    # 4 x 33 x 128 x 128 x 16 bytes = 33 MiB > 32 MiB
+    assert call(4, 33, 128) == 2 and "scratch" in lib.gdn_last_error().decode()
+    assert call(1, 129, 128) == 2
+    # d_k != d_v, and a bad checkpoint list, are refused like the split prefill's
+    sh = gdn._Shape(B=1, H=1, dk=64, dv=128, dtype=1, flags=1)
+    off = gdn._i64([0, n])
+    pos = gdn._i64([n])
+    assert lib.gdn_prefill_emit_checkpoints_split_noalloc(ctypes.byref(sh), p, p, p, p, p, gdn._p64(off), None,
+                                                          gdn._p64(pos), 1, ck, st, p, None) == 2
+    sh = gdn._Shape(B=1, H=1, dk=128, dv=128, dtype=1, flags=1)
+    bad = gdn._i64([n + 1])
+    assert lib.gdn_prefill_emit_checkpoints_split_noalloc(ctypes.byref(sh), p, p, p, p, p, gdn._p64(off), None,
+                                                          gdn._p64(bad), 1, ck, st, p, None) == 1
