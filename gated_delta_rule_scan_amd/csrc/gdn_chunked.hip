@@ -97,17 +97,20 @@ constexpr float kSigMax = 96.f;  // largest state exponent sigma kept between ch
 
 struct Smem {
     alignas(16) _Float16 kh[2][C * KS];  // unit keys, fp16 (layout: krow and the column order below)
-    alignas(16) _Float16 qh[2][C * KS];  // q^ (or q / 2^E), fp16 (same layout)
+    alignas(16) _Float16 qh[2][C * KS];  // q' (q as stored, or q / 2^E), fp16 (same layout)
     alignas(16) uint16_t kqr[2][C * DK];  // raw bf16 keys, queries of the chunk after next: [token][column]
     alignas(16) uint16_t vr[NVB][NW][C * 32];  // raw bf16 v: [wave][token][32 value columns]
     alignas(16) _Float16 tT[2][C * C];   // (T diag(beta))^T * 2^eT as fp16 hi [0] + lo [1], row s, column t
     alignas(16) _Float16 pT[2][C * C];   // P^T, row s, column t
     alignas(16) float gl[2][C];          // chunk-local prefix sum of log2 alpha (gl[C-1]: the chunk's total)
     alignas(16) float be[2][C];          // beta (0 past the chunk)
+    alignas(16) float eg[2][C];          // 2^{g_t}
+    alignas(16) float ws[2][C];          // 2^{g_C - g_t}
     alignas(16) float ks[2][C];          // 1 / ||k'_t||: scale of the stored key row k'_t (0 past the chunk)
-    alignas(16) float kq[2][C];          // 1, or 2^{E_t} for unnormalised queries
+    alignas(16) float kq[2][C];          // query scale q = kq q': 1/||q'_t|| (normalised queries) or 2^{E_t}
     alignas(16) float cw[NW][4][C];      // per-wave coefficients (see the state side)
-    alignas(16) float4 tpart[2][64];     // T_00, T_11^T tiles (accumulator layout) per lane
+    alignas(16) half8 tpart[2][64];      // T_00, T_11^T tiles (accumulator layout) per lane, fp16 hi (0-3) and lo (4-7)
+    int tflag[2];                        // tile b: kTile* bits (see key_side_tile_out)
     float tsc;                           // 2^{-eT}
 };
 constexpr uint32_t OFF_KH = offsetof(Smem, kh);
@@ -514,12 +517,13 @@ __device__ __forceinline__ float convert_key_row(Smem &sm, uint32_t dst, uint4 r
     return s;
 }
 
-// Queries: converts the 8 columns of one lane as convert_key_row does, either
-// normalised (NORMALISE: q / ||q||, rounded to fp16) or scaled by the power of
-// two 2^-E that brings the row's largest element into [1/2, 1), with 2^E
-// returned in kq_out.
-template <bool NORMALISE>
-__device__ __forceinline__ void convert_row(Smem &sm, uint32_t dst, uint4 raw, bool live, float *kq_out) {
+// Queries used as stored (no GDN_NORMALIZE_Q): converts the 8 columns of one
+// lane scaled by the power of two 2^-E that brings the row's largest element
+// into [1/2, 1) (exact), with 2^E returned in kq_out; stored like
+// convert_key_row.  (Normalised queries take convert_key_row: they are kept
+// as stored too, their 1/||q|| going into per-token coefficients.)
+__device__ __forceinline__ void convert_query_row_scaled(Smem &sm, uint32_t dst, uint4 raw, bool live,
+                                                         float *kq_out) {
     // rows past the chunk hold a copy of a live row (finite); they get scale 0
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
     float f[8];
@@ -528,48 +532,14 @@ __device__ __forceinline__ void convert_row(Smem &sm, uint32_t dst, uint4 raw, b
         f[2 * e] = bflo(wd[e]);
         f[2 * e + 1] = bfhi(wd[e]);
     }
-    float sc;
-    if (NORMALISE) {
-        typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-        float ss = 0.f;
+    float mx = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bf16x2v pr = __builtin_bit_cast(bf16x2v, wd[e]);
-            ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
-        }
-        ss = row16_sum(ss);  // one token row per 16 lanes
-        sc = live ? __builtin_amdgcn_rsqf(ss) : 0.f;
-        // The squared norm of a bf16 row can overflow float32 (||q|| above
-        // ~1.8e19) or underflow it (tiny rows; a zero row gives 0).  Any row
-        // outside [2^-100, 2^100] sends the wave through the exact form: the
-        // row is first scaled by a power of two that brings its largest
-        // element into [1/2, 1), so its squared norm lies in [1/4, d_k] and
-        // 1/||q|| is exact to rounding; a zero row keeps scale 0 (stays zero).
-        if (__builtin_amdgcn_ballot_w64(live && !(ss >= 0x1p-100f && ss <= 0x1p100f)) != 0) {
-            float mx = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
-            mx = row16_max(mx);
-            const int E = __builtin_amdgcn_frexp_expf(mx);  // mx = m 2^E, m in [1/2, 1)
-            float s2 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                f[e] = __builtin_amdgcn_ldexpf(f[e], -E);
-                s2 = fmaf(f[e], f[e], s2);
-            }
-            s2 = row16_sum(s2);
-            sc = (live && s2 > 0.f) ? __builtin_amdgcn_rsqf(s2) : 0.f;
-        }
-    } else {
-        float mx = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
-        mx = row16_max(mx);
-        int E = 0;
-        frexpf(mx, &E);
-        sc = live ? ldexpf(1.f, -E) : 0.f;
-        if (kq_out) *kq_out = ldexpf(1.f, E);
-    }
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+    mx = row16_max(mx);
+    int E = 0;
+    frexpf(mx, &E);
+    const float sc = live ? ldexpf(1.f, -E) : 0.f;
+    *kq_out = ldexpf(1.f, E);
     half4 lo, hi;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -617,9 +587,11 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
             const float ksv = convert_key_row(sm, dst, raw[gi], live);
             if (L.n16 == 0) sm.ks[pb][t] = ksv;
         } else {
-            float kqv = 1.f;
-            convert_row<NORM_Q>(sm, dst, raw[gi], live, &kqv);
-            if (!NORM_Q && L.n16 == 0) sm.kq[pb][t] = kqv;
+            // kq: 1/||q'|| of a normalised query, or the power of two of a query used as stored
+            float kqv;
+            if (NORM_Q) kqv = convert_key_row(sm, dst, raw[gi], live);
+            else convert_query_row_scaled(sm, dst, raw[gi], live, &kqv);
+            if (L.n16 == 0) sm.kq[pb][t] = kqv;
         }
     }
     constexpr int w = W;
@@ -629,8 +601,11 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
         const float av = bf(pf.ga);
         const float lg = live ? log2_(fmaxf(av, 1e-30f)) : 0.f;
         const float gs = scan32(lg);
+        const float gC = lane_val(gs, C - 1);
         if (L.lane < 32) {
             sm.gl[pb][tl] = gs;
+            sm.eg[pb][tl] = exp2_(gs);
+            sm.ws[pb][tl] = exp2_(gC - gs);
         } else {
             sm.be[pb][tl] = live ? bf(pf.gb) : 0.f;
         }
@@ -685,11 +660,15 @@ __device__ __forceinline__ floatx4 f4(half4 x) {
 // The product form gives a first inverse T0 = R - R L R (R the 8 x 8
 // block-diagonal inverse, L the lower-left block); its fp16 intermediates lose
 // accuracy when the keys of the tile are nearly parallel and beta approaches
-// 2 (entries of N^2, N^4 far above those of the inverse).  One Newton step,
+// 2 (entries of N^2, N^4 far above those of the inverse).  For a tile with an
+// entry |A_ts| >= kIll (`ill`, uniform over the wave) one Newton step,
 //     T1 = T0 + T0 E,   E = I - (I + A) T0,
 // with A (float32) applied as an fp16 hi/lo pair and T0 exact in fp16,
-// squares the relative error of T0.
-__device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, const Lane &L) {
+// squares the relative error of T0.  Below kIll the fp16 product form is
+// already within about 1.3e-4 (relative Frobenius) of the exact inverse, less
+// than one fp16 rounding of T, so the step is skipped.
+constexpr float kIll = 0.5f;
+__device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, const Lane &L, bool &ill) {
     const int c = L.n16, rb = 4 * L.g;
     half8 f[4];
     task_frags(sm, OFF_KH + pb * KBUF, b ? L.task[1] : L.task[0], f);
@@ -730,6 +709,12 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
         Lw[j] = (lower && !same8) ? val : 0.f;
         Lt[j] = (upper && !same8) ? val : 0.f;
     }
+    {
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) am = fmaxf(am, fmaxf(fabsf(N[j]), fabsf(Lw[j])));
+        ill = __builtin_amdgcn_ballot_w64(am >= kIll) != 0;
+    }
     const half4 Nh = h4(N), Nth = h4(Nt), Lh = h4(Lw), Lth = h4(Lt);
     const floatx4 N2 = mm16(Nth, Nh, z);     // N N
     const floatx4 N2t = mm16(Nh, Nth, z);    // N^T N^T
@@ -740,15 +725,18 @@ __device__ __forceinline__ floatx4 key_side_tile(const Smem &sm, int pb, int b, 
     const floatx4 R1t = mm16(id4 - Nh, id4 + N2th, z);  // (I - N^T)(I + (N^2)^T)
     const floatx4 R = mm16(id4 + h4(N4t), h4(R1), z);   // (I + N^4) R1 = blockdiag inverse
     const floatx4 Rt = mm16(id4 + h4(N4), h4(R1t), z);  // its transpose
-    // T0 and T0^T (accumulator layout), R - R L R
+    // T0 and T0^T (accumulator layout), R - R L R; the copy not returned is
+    // formed only for the Newton step
     floatx4 T0, T0t;
     if (b == 0) {
         const half4 X = h4(mm16(Lth, h4(R), z));  // L R
         T0 = mm16(h4(Rt), -X, R);
+        if (!ill) return T0;
         T0t = mm16(X, -h4(Rt), Rt);
     } else {
         const half4 Xt = h4(mm16(Lh, h4(Rt), z));  // (R L)^T
         T0t = mm16(h4(R), -Xt, Rt);
+        if (!ill) return T0t;
         T0 = mm16(Xt, -h4(R), R);
     }
     const half4 T0h = h4(T0), T0th = h4(T0t);
@@ -792,73 +780,148 @@ __device__ __forceinline__ floatx4 key_side_a10t(const Smem &sm, int pb, const L
     return A10t;
 }
 
-// Combine (one wave): T_10 = -T_11 A_10 T_00, then T diag(beta) scaled into
-// the fp16 band and stored as an fp16 hi/lo pair (row s, column t).  Both
-// products take their operands as hi/lo pairs (three MFMAs each: hi hi,
-// lo hi, hi lo), so that T keeps float32 accuracy up to the state update.
-// A10t: A_10^T of the chunk, kept in this wave's registers since its task.
-__device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L, const floatx4 &A10t) {
-    const int lane = L.lane;
-    const float4 a = sm.tpart[0][lane], bq = sm.tpart[1][lane];
-    const floatx4 T00 = {a.x, a.y, a.z, a.w}, T11t = {bq.x, bq.y, bq.z, bq.w};
-    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-    half4 ah, al, th, tl;
-    split16(A10t, ah, al);
-    split16(T00, th, tl);
-    floatx4 W = mm16(ah, th, z);  // A_10 T_00
-    W = mm16(al, th, W);
-    W = mm16(ah, tl, W);
-    half4 wh, wl, uh, ul;
-    split16(-W, wh, wl);
-    split16(T11t, uh, ul);
-    floatx4 T10 = mm16(uh, wh, z);  // -T_11 (A_10 T_00)
-    T10 = mm16(ul, wh, T10);
-    T10 = mm16(uh, wl, T10);
-    const int c = L.n16, rb = 4 * L.g;
-    const float *be = sm.be[pb];
-    const float bs0 = be[c];
-    const float4 b14 = *reinterpret_cast<const float4 *>(&be[16 + rb]);
-    const float b1v[4] = {b14.x, b14.y, b14.z, b14.w};
-    floatx4 t00, t10, t11;
-    float mx = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        t00[j] = T00[j] * bs0;
-        t10[j] = T10[j] * bs0;
-        t11[j] = T11t[j] * b1v[j];
-        mx = fmaxf(mx, fmaxf(fabsf(t00[j]), fmaxf(fabsf(t10[j]), fabsf(t11[j]))));
-    }
-    const int eT = out_of_band(mx) ? f16_adjust(wave_max(mx)) : 0;
-    if (eT != 0) {
-        const float sc = ldexpf(1.f, eT);
-        t00 *= sc;
-        t10 *= sc;
-        t11 *= sc;
-    }
-    half4 h00, l00, h10, l10, h11, l11;
-    split16(t00, h00, l00);
-    split16(t10, h10, l10);
-    split16(t11, h11, l11);
+// Stores a 4-element part of T diag(beta) (accumulator layout) as its fp16
+// hi/lo pair: block 0 = T_00 (rows t = rb + j, column s = c), 1 = T_10
+// (t = 16 + rb + j, s = c), 2 = T_11 held transposed (t = 16 + c, s = 16 + rb + j).
+// Stored as (row s, column t).
+// split = false stores x rounded once, with a zero lo part.
+__device__ __forceinline__ void store_tpart(Smem &sm, int blk, const floatx4 &x, int c, int rb, bool split = true) {
+    half4 hi, lo = {0, 0, 0, 0};
+    if (split) split16(x, hi, lo);
+    else hi = h4(x);
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
         _Float16 *tt = sm.tT[part];
-        const half4 x00 = part ? l00 : h00, x10 = part ? l10 : h10, x11 = part ? l11 : h11;
-        *reinterpret_cast<half4 *>(&tt[c * C + rb]) = x00;        // t = rb + j, s = c
-        *reinterpret_cast<half4 *>(&tt[c * C + 16 + rb]) = x10;   // t = 16 + rb + j, s = c
+        const half4 v = part ? lo : hi;
+        if (blk == 0) {
+            *reinterpret_cast<half4 *>(&tt[c * C + rb]) = v;
+        } else if (blk == 1) {
+            *reinterpret_cast<half4 *>(&tt[c * C + 16 + rb]) = v;
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tt[(16 + rb + j) * C + 16 + c] = x11[j];  // t = 16 + c, s = 16 + rb + j
+            for (int j = 0; j < 4; ++j) tt[(16 + rb + j) * C + 16 + c] = v[j];
+        }
     }
+}
+
+// Flags of a diagonal tile for the combine (LDS tflag).
+constexpr int kTileHigh = 1;  // some |T_bb diag(beta)| >= 2^14
+constexpr int kTileLow = 2;   // every |T_bb diag(beta)| < 2^-6
+constexpr int kTileIll = 4;   // the tile took the Newton step (an |A_ts| >= kIll)
+
+// Diagonal tile b (wave 0: b = 0, wave 2: b = 1) after key_side_tile: keeps the
+// tile for the combine (fp16 hi, and lo when ill), and stores its block of
+// T diag(beta) unscaled, as an fp16 hi/lo pair when ill and as a single fp16
+// value with a zero lo part otherwise (a well-conditioned T is exact to one
+// fp16 rounding anyway), with flags for the combine's split decision and range
+// check (it rescales all of T in the rare case that T diag(beta) leaves the
+// fp16 band).
+__device__ __forceinline__ void key_side_tile_out(Smem &sm, int pb, int b, const floatx4 &r, bool ill,
+                                                  const Lane &L) {
+    const int c = L.n16, rb = 4 * L.g;
+    const half4 zero4 = {0, 0, 0, 0};
+    half4 hi, lo = zero4;
+    if (ill) split16(r, hi, lo);
+    else hi = h4(r);
+    sm.tpart[b][L.lane] = cat(hi, lo);
+    floatx4 x;
+    if (b == 0) {
+        const float bs = sm.be[pb][c];  // column s = c
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = r[j] * bs;
+    } else {
+        const float4 b4 = *reinterpret_cast<const float4 *>(&sm.be[pb][16 + rb]);  // columns s = 16 + rb + j
+        x[0] = r[0] * b4.x; x[1] = r[1] * b4.y; x[2] = r[2] * b4.z; x[3] = r[3] * b4.w;
+    }
+    store_tpart(sm, b ? 2 : 0, x, c, rb, ill);
+    const float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    const bool high = __builtin_amdgcn_ballot_w64(mx >= 0x1p14f) != 0;
+    const bool low = __builtin_amdgcn_ballot_w64(mx >= 0x1p-6f) == 0;
+    if (L.lane == 0) sm.tflag[b] = (high ? kTileHigh : 0) | (low ? kTileLow : 0) | (ill ? kTileIll : 0);
+}
+
+// Combine (one wave): T_10 = -T_11 A_10 T_00, its block of T diag(beta)
+// stored as an fp16 hi/lo pair next to the diagonal blocks.  When a tile took
+// the Newton step or A_10 has an entry >= kIll, both products take their
+// operands as hi/lo pairs (three MFMAs each: hi hi, lo hi, hi lo), so that T
+// keeps float32 accuracy up to the state update; otherwise single fp16
+// products are exact to one rounding of T.  If T diag(beta) as a whole leaves
+// the fp16 band, all three blocks are rescaled by a power of two 2^eT
+// (tsc = 2^-eT).
+// A10t: A_10^T of the chunk, kept in this wave's registers since its task.
+__device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L, const floatx4 &A10t) {
+    const int lane = L.lane;
+    const half8 p0 = sm.tpart[0][lane], p1 = sm.tpart[1][lane];
+    const int f0 = sm.tflag[0], f1 = sm.tflag[1];
+    const half4 th = __builtin_shufflevector(p0, p0, 0, 1, 2, 3), tl = __builtin_shufflevector(p0, p0, 4, 5, 6, 7);
+    const half4 uh = __builtin_shufflevector(p1, p1, 0, 1, 2, 3), ul = __builtin_shufflevector(p1, p1, 4, 5, 6, 7);
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) am = fmaxf(am, fabsf(A10t[j]));
+    const bool ill = ((f0 | f1) & kTileIll) != 0 || __builtin_amdgcn_ballot_w64(am >= kIll) != 0;
+    floatx4 T10;
+    if (ill) {
+        const half4 zero4 = {0, 0, 0, 0};
+        const half4 tl0 = (f0 & kTileIll) ? tl : zero4, ul0 = (f1 & kTileIll) ? ul : zero4;
+        half4 ah, al;
+        split16(A10t, ah, al);
+        floatx4 W = mm16(ah, th, z);  // A_10 T_00
+        W = mm16(al, th, W);
+        W = mm16(ah, tl0, W);
+        half4 wh, wl;
+        split16(-W, wh, wl);
+        T10 = mm16(uh, wh, z);  // -T_11 (A_10 T_00)
+        T10 = mm16(ul0, wh, T10);
+        T10 = mm16(uh, wl, T10);
+    } else {
+        const floatx4 W = mm16(h4(A10t), th, z);
+        T10 = mm16(uh, -h4(W), z);
+    }
+    const int c = L.n16, rb = 4 * L.g;
+    const float bs0 = sm.be[pb][c];
+    floatx4 t10;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t10[j] = T10[j] * bs0;
+    const float mx = fmaxf(fmaxf(fabsf(t10[0]), fabsf(t10[1])), fmaxf(fabsf(t10[2]), fabsf(t10[3])));
+    const bool high = ((f0 | f1) & kTileHigh) != 0 || __builtin_amdgcn_ballot_w64(mx >= 0x1p14f) != 0;
+    const bool low = (f0 & f1 & kTileLow) != 0 && __builtin_amdgcn_ballot_w64(mx >= 0x1p-6f) == 0;
+    if (!high && !low) {
+        store_tpart(sm, 1, t10, c, rb, ill);
+        if (lane == 0) sm.tsc = 1.f;
+        return;
+    }
+    // rare: rescale every block (the diagonal ones rebuilt from their hi/lo pairs)
+    const float4 b14 = *reinterpret_cast<const float4 *>(&sm.be[pb][16 + rb]);
+    const float b1v[4] = {b14.x, b14.y, b14.z, b14.w};
+    floatx4 t00, t11;
+    float m2 = mx;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        t00[j] = ((float)th[j] + ((f0 & kTileIll) ? (float)tl[j] : 0.f)) * bs0;
+        t11[j] = ((float)uh[j] + ((f1 & kTileIll) ? (float)ul[j] : 0.f)) * b1v[j];
+        m2 = fmaxf(m2, fmaxf(fabsf(t00[j]), fabsf(t11[j])));
+    }
+    const int eT = f16_adjust(wave_max(m2));
+    const float sc = ldexpf(1.f, eT);
+    store_tpart(sm, 0, t00 * sc, c, rb);
+    store_tpart(sm, 1, t10 * sc, c, rb);
+    store_tpart(sm, 2, t11 * sc, c, rb);
     if (lane == 0) sm.tsc = ldexpf(1.f, -eT);
 }
 
 // ---- key side, part 3 (wave 1): P -> fp16, transposed -------------------------
+// NORM_Q: the queries' scales 1/||q'|| go into the rows of P (queries used as
+// stored keep theirs in the output coefficients instead, where a large scale
+// cannot overflow fp16).  QFROMK: the query tile is the key tile (q = k).
+template <bool NORM_Q, bool QFROMK>
 __device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
     const int c = L.n16, rb = 4 * L.g;
     half8 k0[4], k1[4], q0[4], q1[4];
     task_frags(sm, OFF_KH + pb * KBUF, L.task[0], k0);
     task_frags(sm, OFF_KH + pb * KBUF, L.task[1], k1);
-    task_frags(sm, OFF_QH + pb * KBUF, L.task[0], q0);
-    task_frags(sm, OFF_QH + pb * KBUF, L.task[1], q1);
+    task_frags(sm, (QFROMK ? OFF_KH : OFF_QH) + pb * KBUF, L.task[0], q0);
+    task_frags(sm, (QFROMK ? OFF_KH : OFF_QH) + pb * KBUF, L.task[1], q1);
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
     floatx4 P00 = z, P10 = z, P11 = z;
 #pragma unroll
@@ -873,13 +936,22 @@ __device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
     const float4 a4 = *reinterpret_cast<const float4 *>(&gl[rb]);
     const float4 b4 = *reinterpret_cast<const float4 *>(&gl[16 + rb]);
     const float gt0[4] = {a4.x, a4.y, a4.z, a4.w}, gt1[4] = {b4.x, b4.y, b4.z, b4.w};
+    float qs0[4] = {1.f, 1.f, 1.f, 1.f}, qs1[4] = {1.f, 1.f, 1.f, 1.f};
+    if (NORM_Q) {
+        const float *qsc = QFROMK ? sm.ks[pb] : sm.kq[pb];
+        const float4 u4 = *reinterpret_cast<const float4 *>(&qsc[rb]);
+        const float4 w4 = *reinterpret_cast<const float4 *>(&qsc[16 + rb]);
+        qs0[0] = u4.x; qs0[1] = u4.y; qs0[2] = u4.z; qs0[3] = u4.w;
+        qs1[0] = w4.x; qs1[1] = w4.y; qs1[2] = w4.z; qs1[3] = w4.w;
+    }
     floatx4 x00, x10, x11;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = rb + j;
-        const float e00 = exp2_(gt0[j] - g0) * ks0 * P00[j], e11 = exp2_(gt1[j] - g1) * ks1 * P11[j];
+        const float e00 = exp2_(gt0[j] - g0) * (ks0 * qs0[j]) * P00[j];
+        const float e11 = exp2_(gt1[j] - g1) * (ks1 * qs1[j]) * P11[j];
         x00[j] = c <= r ? e00 : 0.f;
-        x10[j] = exp2_(gt1[j] - g0) * ks0 * P10[j];
+        x10[j] = exp2_(gt1[j] - g0) * (ks0 * qs1[j]) * P10[j];
         x11[j] = c <= r ? e11 : 0.f;
     }
     _Float16 *pt = sm.pT[pb];
@@ -891,18 +963,19 @@ __device__ __forceinline__ void key_side_P(Smem &sm, int pb, const Lane &L) {
 // Key-side tasks of one chunk after its conversion: wave 0 tile 0, wave 2
 // tile 1, wave 3 A_10^T (kept in its registers, a10t, for its own combine),
 // wave 1 P.
-template <bool WANT_O>
+template <bool WANT_O, bool NORM_Q, bool QFROMK>
 __device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, const Lane &L, floatx4 &a10t) {
     if (w == 1) {
-        if (WANT_O) key_side_P(sm, pb, L);
+        if (WANT_O) key_side_P<NORM_Q, QFROMK>(sm, pb, L);
         return;
     }
     if (w == 3) {
         a10t = key_side_a10t(sm, pb, L);
         return;
     }
-    const floatx4 r = key_side_tile(sm, pb, w >> 1, L);
-    sm.tpart[w >> 1][L.lane] = make_float4(r[0], r[1], r[2], r[3]);
+    bool ill;
+    const floatx4 r = key_side_tile(sm, pb, w >> 1, L, ill);
+    key_side_tile_out(sm, pb, w >> 1, r, ill, L);
 }
 
 // ---- state-side operand reads ---------------------------------------------------
@@ -959,6 +1032,9 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     // every wave does both.  Both groups pass the same barriers.
     constexpr bool STATE = !SPLIT || ROLE < 4;
     constexpr bool KEY = !SPLIT || ROLE >= 4;
+    // q = k = v, both normalised: the stored query rows are the stored key rows,
+    // so the key tile and its scales serve as the query tile and query scales
+    constexpr bool QFROMK = ALIAS && NORM_Q;
 
     const int Lg = xcd_remap(blockIdx.x, gridDim.x);
     const int h = Lg % P.H;
@@ -1077,7 +1153,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     lds_barrier();
     if (cur.lc > 0) {
         if (KEY) {
-            if (ALIAS) key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L, OFF_KQR, OFF_KQR);
+            if (ALIAS) key_side_convert<WANT_O && !QFROMK, NORM_Q, w>(sm, 0, pf, cur.lc, L, OFF_KQR, OFF_KQR);
             else key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
         }
         lds_barrier();  // the raw tiles are free again (ALIAS: tile 0 keeps chunk 0's values)
@@ -1085,7 +1161,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L, ALIAS ? RAW1 : OFF_KQR);
             load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
         }
-        if (KEY) key_side_tasks<WANT_O>(sm, 0, w, L, a10t);
+        if (KEY) key_side_tasks<WANT_O, NORM_Q, QFROMK>(sm, 0, w, L, a10t);
     }
 
     int p = 0;   // key-side buffer of the current chunk
@@ -1121,7 +1197,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         if (KEY && nx.lc > 0) {
             if (ALIAS) {
                 const uint32_t rawn = kp ? OFF_KQR : RAW1;  // raw tile of `nx`
-                key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L, rawn, rawn);
+                key_side_convert<WANT_O && !QFROMK, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L, rawn, rawn);
             } else {
                 key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
             }
@@ -1139,7 +1215,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             kf[m] = lds_ld<half8>(sm, kbuf + L.yz + 32 * m);
-            if (WANT_O) qf[m] = lds_ld<half8>(sm, kbuf + 2 * KBUF + L.yz + 32 * m);
+            if (WANT_O) qf[m] = lds_ld<half8>(sm, kbuf + (QFROMK ? 0 : 2 * KBUF) + L.yz + 32 * m);
         }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -1157,16 +1233,15 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         }
         const float isg = exp2_(-sigma);
         if (lane < 32) {
-            const float glt = sm.gl[p][lane];
-            const float e = exp2_(glt);          // 2^{g_t}
-            const float kq = NORM_Q ? 1.f : sm.kq[p][lane];
+            const float e = sm.eg[p][lane];      // 2^{g_t}
             const float kst = sm.ks[p][lane];    // k^_t = kst k'_t
+            const float kq = QFROMK ? kst : sm.kq[p][lane];  // q^_t (or q_t) = kq q'_t
             cwl[lane] = e * isg * kst;           // B~ = v - cw0 Y', Y' = K' Sacc^T
             if (WANT_O) cwl[C + lane] = kq * e * isg;  // o (state part) = cw1 Z
             // W' = cw2 U (rows of K'^T W' = K^^T W) and o (intra part) = cw3 (P U'),
             // for unscaled T, B~, U and no rescale of the state (rewritten below
             // otherwise): 2^{g_C - g_t} 2^{sigma - g_C} kst
-            cwl[2 * C + lane] = exp2_(sigma - glt) * kst;
+            cwl[2 * C + lane] = sm.ws[p][lane] * exp2_(sigma - sm.gl[p][C - 1]) * kst;
             if (WANT_O && !NORM_Q) cwl[3 * C + lane] = kq;
         }
         // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
@@ -1216,7 +1291,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
                 dma_v_all(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L);
             }
             if (w != 3) __builtin_amdgcn_s_setprio(1);  // the longer tasks of this phase go first
-            if (nx.lc > 0) key_side_tasks<WANT_O>(sm, p ^ 1, w, L, a10t);
+            if (nx.lc > 0) key_side_tasks<WANT_O, NORM_Q, QFROMK>(sm, p ^ 1, w, L, a10t);
             if (w != 3) __builtin_amdgcn_s_setprio(0);
             if (!EARLY) load_kq<1, WANT_O && !ALIAS>(pf, sm_lds, G, kt2, klc2, w, L);
         };
@@ -1225,7 +1300,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         // operands of `cur` that are complete now are read before the tasks
         const half8 tfr0 = tr_frag_st(sm, OFF_TT, 0, L);
         const half8 tfr1 = tr_frag_st(sm, OFF_TT, 1, L);
-        const half8 tfl0 = tr_frag_st(sm, OFF_TT + C * C * 2, 0, L);  // lo part of T
+        const half8 tfl0 = tr_frag_st(sm, OFF_TT + C * C * 2, 0, L);  // lo part of T (zero unless refined)
         const half8 tfl1 = tr_frag_st(sm, OFF_TT + C * C * 2, 1, L);
         half8 pfr0, pfr1;
         if (WANT_O) {
