@@ -110,7 +110,7 @@ struct Smem {
     alignas(16) float kq[2][C];          // query scale q = kq q': 1/||q'_t|| (normalised queries) or 2^{E_t}
     alignas(16) float cw[NW][4][C];      // per-wave coefficients (see the state side)
     alignas(16) half8 tpart[2][64];      // T_00, T_11^T tiles (accumulator layout) per lane, fp16 hi (0-3) and lo (4-7)
-    int tflag[2];                        // tile b: kTile* bits (see key_side_tile_out)
+    int tflag[2];                        // tile b: kTileIll (see key_side_tile_out)
     float tsc;                           // 2^{-eT}
 };
 constexpr uint32_t OFF_KH = offsetof(Smem, kh);
@@ -804,50 +804,28 @@ __device__ __forceinline__ void store_tpart(Smem &sm, int blk, const floatx4 &x,
     }
 }
 
-// Flags of a diagonal tile for the combine (LDS tflag).
-constexpr int kTileHigh = 1;  // some |T_bb diag(beta)| >= 2^14
-constexpr int kTileLow = 2;   // every |T_bb diag(beta)| < 2^-6
-constexpr int kTileIll = 4;   // the tile took the Newton step (an |A_ts| >= kIll)
+// Flag of a diagonal tile for the combine (LDS tflag): the tile took the
+// Newton step (an |A_ts| >= kIll), so its staged copy carries a lo part.
+constexpr int kTileIll = 4;
 
-// Diagonal tile b (wave 0: b = 0, wave 2: b = 1) after key_side_tile: keeps the
-// tile for the combine (fp16 hi, and lo when ill), and stores its block of
-// T diag(beta) unscaled, as an fp16 hi/lo pair when ill and as a single fp16
-// value with a zero lo part otherwise (a well-conditioned T is exact to one
-// fp16 rounding anyway), with flags for the combine's split decision and range
-// check (it rescales all of T in the rare case that T diag(beta) leaves the
-// fp16 band).
-__device__ __forceinline__ void key_side_tile_out(Smem &sm, int pb, int b, const floatx4 &r, bool ill,
-                                                  const Lane &L) {
-    const int c = L.n16, rb = 4 * L.g;
-    const half4 zero4 = {0, 0, 0, 0};
-    half4 hi, lo = zero4;
+// Diagonal tile b (wave 0: b = 0, wave 2: b = 1) after key_side_tile: stages
+// the tile for the combine, fp16 hi and (when ill) lo.  The tile's block of
+// T diag(beta) is written by the combine, in the next phase: the state side
+// still reads the current chunk's T during this one.
+__device__ __forceinline__ void key_side_tile_out(Smem &sm, int b, const floatx4 &r, bool ill, const Lane &L) {
+    half4 hi, lo = {0, 0, 0, 0};
     if (ill) split16(r, hi, lo);
     else hi = h4(r);
     sm.tpart[b][L.lane] = cat(hi, lo);
-    floatx4 x;
-    if (b == 0) {
-        const float bs = sm.be[pb][c];  // column s = c
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = r[j] * bs;
-    } else {
-        const float4 b4 = *reinterpret_cast<const float4 *>(&sm.be[pb][16 + rb]);  // columns s = 16 + rb + j
-        x[0] = r[0] * b4.x; x[1] = r[1] * b4.y; x[2] = r[2] * b4.z; x[3] = r[3] * b4.w;
-    }
-    store_tpart(sm, b ? 2 : 0, x, c, rb, ill);
-    const float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-    const bool high = __builtin_amdgcn_ballot_w64(mx >= 0x1p14f) != 0;
-    const bool low = __builtin_amdgcn_ballot_w64(mx >= 0x1p-6f) == 0;
-    if (L.lane == 0) sm.tflag[b] = (high ? kTileHigh : 0) | (low ? kTileLow : 0) | (ill ? kTileIll : 0);
+    if (L.lane == 0) sm.tflag[b] = ill ? kTileIll : 0;
 }
 
-// Combine (one wave): T_10 = -T_11 A_10 T_00, its block of T diag(beta)
-// stored as an fp16 hi/lo pair next to the diagonal blocks.  When a tile took
-// the Newton step or A_10 has an entry >= kIll, both products take their
-// operands as hi/lo pairs (three MFMAs each: hi hi, lo hi, hi lo), so that T
+// Combine (one wave): T_10 = -T_11 A_10 T_00, then T diag(beta) scaled into
+// the fp16 band and stored (row s, column t) as an fp16 hi/lo pair.  When a
+// tile took the Newton step or A_10 has an entry >= kIll, both products take
+// their operands as hi/lo pairs (three MFMAs each: hi hi, lo hi, hi lo) and T
 // keeps float32 accuracy up to the state update; otherwise single fp16
-// products are exact to one rounding of T.  If T diag(beta) as a whole leaves
-// the fp16 band, all three blocks are rescaled by a power of two 2^eT
-// (tsc = 2^-eT).
+// products and a single fp16 T (zero lo part) are exact to one rounding of T.
 // A10t: A_10^T of the chunk, kept in this wave's registers since its task.
 __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L, const floatx4 &A10t) {
     const int lane = L.lane;
@@ -862,51 +840,43 @@ __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L
     const bool ill = ((f0 | f1) & kTileIll) != 0 || __builtin_amdgcn_ballot_w64(am >= kIll) != 0;
     floatx4 T10;
     if (ill) {
-        const half4 zero4 = {0, 0, 0, 0};
-        const half4 tl0 = (f0 & kTileIll) ? tl : zero4, ul0 = (f1 & kTileIll) ? ul : zero4;
         half4 ah, al;
         split16(A10t, ah, al);
-        floatx4 W = mm16(ah, th, z);  // A_10 T_00
+        floatx4 W = mm16(ah, th, z);  // A_10 T_00 (a tile without the step has lo = 0)
         W = mm16(al, th, W);
-        W = mm16(ah, tl0, W);
+        W = mm16(ah, tl, W);
         half4 wh, wl;
         split16(-W, wh, wl);
         T10 = mm16(uh, wh, z);  // -T_11 (A_10 T_00)
-        T10 = mm16(ul0, wh, T10);
+        T10 = mm16(ul, wh, T10);
         T10 = mm16(uh, wl, T10);
     } else {
         const floatx4 W = mm16(h4(A10t), th, z);
         T10 = mm16(uh, -h4(W), z);
     }
     const int c = L.n16, rb = 4 * L.g;
-    const float bs0 = sm.be[pb][c];
-    floatx4 t10;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t10[j] = T10[j] * bs0;
-    const float mx = fmaxf(fmaxf(fabsf(t10[0]), fabsf(t10[1])), fmaxf(fabsf(t10[2]), fabsf(t10[3])));
-    const bool high = ((f0 | f1) & kTileHigh) != 0 || __builtin_amdgcn_ballot_w64(mx >= 0x1p14f) != 0;
-    const bool low = (f0 & f1 & kTileLow) != 0 && __builtin_amdgcn_ballot_w64(mx >= 0x1p-6f) == 0;
-    if (!high && !low) {
-        store_tpart(sm, 1, t10, c, rb, ill);
-        if (lane == 0) sm.tsc = 1.f;
-        return;
-    }
-    // rare: rescale every block (the diagonal ones rebuilt from their hi/lo pairs)
-    const float4 b14 = *reinterpret_cast<const float4 *>(&sm.be[pb][16 + rb]);
+    const float bs0 = sm.be[pb][c];  // column s = c (T_00, T_10)
+    const float4 b14 = *reinterpret_cast<const float4 *>(&sm.be[pb][16 + rb]);  // columns s = 16 + rb + j (T_11^T)
     const float b1v[4] = {b14.x, b14.y, b14.z, b14.w};
-    floatx4 t00, t11;
-    float m2 = mx;
+    floatx4 t00, t10, t11;
+    float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        t00[j] = ((float)th[j] + ((f0 & kTileIll) ? (float)tl[j] : 0.f)) * bs0;
-        t11[j] = ((float)uh[j] + ((f1 & kTileIll) ? (float)ul[j] : 0.f)) * b1v[j];
-        m2 = fmaxf(m2, fmaxf(fabsf(t00[j]), fabsf(t11[j])));
+        t00[j] = ((float)th[j] + (float)tl[j]) * bs0;
+        t10[j] = T10[j] * bs0;
+        t11[j] = ((float)uh[j] + (float)ul[j]) * b1v[j];
+        mx = fmaxf(mx, fmaxf(fabsf(t00[j]), fmaxf(fabsf(t10[j]), fabsf(t11[j]))));
     }
-    const int eT = f16_adjust(wave_max(m2));
-    const float sc = ldexpf(1.f, eT);
-    store_tpart(sm, 0, t00 * sc, c, rb);
-    store_tpart(sm, 1, t10 * sc, c, rb);
-    store_tpart(sm, 2, t11 * sc, c, rb);
+    const int eT = out_of_band(mx) ? f16_adjust(wave_max(mx)) : 0;
+    if (eT != 0) {
+        const float sc = ldexpf(1.f, eT);
+        t00 *= sc;
+        t10 *= sc;
+        t11 *= sc;
+    }
+    store_tpart(sm, 0, t00, c, rb, ill);
+    store_tpart(sm, 1, t10, c, rb, ill);
+    store_tpart(sm, 2, t11, c, rb, ill);
     if (lane == 0) sm.tsc = ldexpf(1.f, -eT);
 }
 
@@ -975,7 +945,7 @@ __device__ __forceinline__ void key_side_tasks(Smem &sm, int pb, int w, const La
     }
     bool ill;
     const floatx4 r = key_side_tile(sm, pb, w >> 1, L, ill);
-    key_side_tile_out(sm, pb, w >> 1, r, ill, L);
+    key_side_tile_out(sm, w >> 1, r, ill, L);
 }
 
 // ---- state-side operand reads ---------------------------------------------------
