@@ -1427,6 +1427,408 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     if (STATE && P.state_dst[r]) store_state(P.state_dst[r] + (int64_t)h * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
+// ---- d_v in two halves --------------------------------------------------------
+// A launch that leaves half of the CUs idle gives each (request, head) two
+// workgroups of eight waves, one per half of its d_v = 128 value rows: the
+// rows of S do not interact (the key operator of eq. (1) acts from the right).
+// Waves 4-7 run the key side exactly as the eight-wave kernel does (both
+// halves form the same T and P; their key and gate rows are read by two
+// workgroups of one XCD).  Waves 0-3 each own 16 value rows of the half and
+// run the state side on v_mfma_f32_16x16x32_f16, so that each wave's share of
+// every state product is half that of the eight-wave kernel.
+//
+// State wave w of half hv, lane (g, n) = (lane / 16, lane % 16), value row
+// dvr = 64 hv + 16 w + n:
+//  - S^T is held as 8 accumulator tiles of 16 stored key columns; tile a,
+//    accumulator row 4 g' + j covers the stored column 32 (a/2) + 8 g' + 4 (a%2) + j,
+//    so that tiles 2m and 2m+1 of a lane make one 8-element B fragment of the
+//    stored columns 32 m + 8 g .. +7, i.e. one 16-byte read of a key row;
+//  - Y = K S^T, B~, U and W' (lane: value column n, tokens 16 tb + 4 g + j);
+//    Z^T = S Q^T and O^T (lane: token 16 tt + n, value columns 4 g + j), so
+//    that a lane stores 4 consecutive outputs as 8 bytes;
+//  - K^T, T and P as A / B operands in the token order of U's tiles (s = 4 g + j
+//    and 16 + 4 g + j) come from transposed reads of the token-major tiles.
+// V of a chunk: 32 rows of the half's 64 columns (128 bytes) per buffer, the
+// 16-byte slot u of row t holding the row's unit u ^ 2 ((t / 2) % 4) (the
+// transposed B~ reads are then free of bank conflicts).
+constexpr uint32_t V2BUF = C * 128;  // bytes of one V buffer
+static_assert(NVB * V2BUF <= sizeof(Smem::vr), "V buffers of the split kernel fit the V staging area");
+
+struct Lane2 {
+    uint32_t yz;     // Y / Z fragments: row krow(n), stored column 8 g (+64 bytes per k-step, +16 rows per token tile)
+    uint32_t vrd;    // transposed V reads of token tile 0 (+2048 bytes for tile 1)
+    uint32_t st;     // transposed T / P reads of s = 4 g + (n / 4), t = 4 (n % 4) (+32 bytes per t tile, +1024 for s + 16)
+    uint32_t kt[2];  // transposed K^T reads, s = 4 g + n / 4 (+16 for kt[1]), stored column 8 (n % 4)
+    uint32_t vcol;   // V copies: the lane's 16-byte unit of a row (swizzled)
+    int scol;        // logical key column of accumulator row 4 g of tile 0 (+32 (a/2) + 8 (a%2))
+};
+__device__ __forceinline__ Lane2 make_lane2(int lane, int w) {
+    const int g = lane >> 4, n = lane & 15;
+    Lane2 L;
+    L.yz = krow(n) * KROWB + 16 * g;
+    L.vrd = (4 * g + (n >> 2)) * 128 + 16 * ((2 * w + ((n & 3) >> 1)) ^ (2 * ((2 * g + (n >> 3)) & 3))) + 8 * (n & 1);
+    L.st = (4 * g + (n >> 2)) * 64 + 8 * (n & 3);
+    L.kt[0] = krow(4 * g + (n >> 2)) * KROWB + 16 * (n & 3);
+    L.kt[1] = krow(16 + 4 * g + (n >> 2)) * KROWB + 16 * (n & 3);
+    L.vcol = 16 * ((lane & 7) ^ (2 * ((lane >> 4) & 3)));
+    // stored column 32 m + 8 g + 4 h + j is the key column 32 m + 16 (g/2) + 8 h + 4 (g%2) + j
+    L.scol = 16 * (g >> 1) + 4 * (g & 1);
+    return L;
+}
+
+// V rows 8 i .. 8 i + 7 of a chunk into buffer vb (1 KiB): lane l writes slot
+// l % 8 of row 8 i + l / 8.  Rows past the chunk are clamped to its last row.
+__device__ __forceinline__ void dma_v2(uint32_t sm_lds, int vb, const Bases &G, int t0, int lc, const Lane2 &L2,
+                                       int lane, int i) {
+    const uint64_t base = at_tok(G.v, t0, G.ts);
+    const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L2.vcol;
+    dma16(base, min((uint32_t)(8 * i + (lane >> 3)) * G.ts + L2.vcol, lim),
+          sm_lds + OFF_VR + (uint32_t)(vb * V2BUF + 1024 * i));
+}
+
+// S = 2^{-sigma} S2 of value row dvr to a d_v x d_k row-major block.
+__device__ __forceinline__ void store_state2(float *dst_head, const floatx4 (&S2)[8], float sigma, int dvr, int scol) {
+    float *dst = dst_head + (int64_t)dvr * DK + scol;
+    const float sc = exp2_(-sigma);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+        *reinterpret_cast<float4 *>(dst + 32 * (a >> 1) + 8 * (a & 1)) =
+            make_float4(S2[a][0] * sc, S2[a][1] * sc, S2[a][2] * sc, S2[a][3] * sc);
+}
+
+// A fragment of a 32 x 32 fp16 matrix X stored as (row s, column t): rows
+// t = 16 tt + n, reduction s in the order 4 g + j, 16 + 4 g + j.
+__device__ __forceinline__ half8 tr_frag2(const Smem &sm, uint32_t mat, int tt, const Lane2 &L2) {
+    const uint32_t o = mat + L2.st + 32 * tt;
+    return cat(tr4(sm, o), tr4(sm, o + 1024));
+}
+
+template <int ROLE, bool WANT_O, bool NORM_Q>
+__device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t sm_lds)
+{
+    constexpr bool STATE = ROLE < 4;
+    constexpr bool KEY = ROLE >= 4;
+    constexpr int w = ROLE & 3;
+
+    const int Lg = xcd_remap(blockIdx.x, gridDim.x);
+    const int hv = Lg & 1;
+    const int pair = Lg >> 1;
+    const int h = pair % P.H;
+    const int r = pair / P.H;
+    const int b = P.req[r];
+    const int H = P.H;
+    const int tid = threadIdx.x;
+    const Lane L = make_lane(tid, w, H);
+    const Lane2 L2 = make_lane2(L.lane, w);
+    const int lane = L.lane, g = L.g, n = L.n16;
+    const int dvr = 64 * hv + 16 * w + n;
+    const int len = P.len[r];
+    const int64_t row0 = P.row0[r];
+    const int ne_end = P.emit_begin[r + 1];
+    const int wf = P.wflags[r];
+    const bool zero_v = (wf & kWorkZeroV) != 0;
+    const bool out = WANT_O && !(wf & kWorkNoOut);
+    Bases G;
+    {
+        const uint64_t th = (uint64_t)(row0 * H + h);
+        G.ts = (uint32_t)(H * DK * 2);
+        G.tg = (uint32_t)(H * 2);
+        G.k = uniform64(reinterpret_cast<uint64_t>(P.k) + th * (DK * 2));
+        G.q = uniform64(reinterpret_cast<uint64_t>(P.q) + th * (DK * 2));
+        G.v = uniform64(reinterpret_cast<uint64_t>(P.v) + th * (DV * 2) + 128 * hv);
+        G.o = uniform64(reinterpret_cast<uint64_t>(P.o) + th * (DV * 2) + 128 * hv);
+        G.a = uniform64(reinterpret_cast<uint64_t>(P.alpha) + th * 2);
+        G.b = uniform64(reinterpret_cast<uint64_t>(P.beta) + th * 2);
+    }
+
+    floatx4 S2[8];
+    float sigma = 0.f;
+    float mb = 0.f;  // bound on max |S2| per value column (lanes n, n + 16, n + 32, n + 48)
+    if (!STATE) {
+    } else if (wf & kWorkIdentity) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S2[a][j] = (32 * (a >> 1) + 8 * (a & 1) + L2.scol + j) == dvr ? 1.f : 0.f;
+    } else if (P.init_off[r] >= 0) {
+        const float *src = P.init_base + P.init_off[r] + (int64_t)h * DV * DK + (int64_t)dvr * DK + L2.scol;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(src + 32 * (a >> 1) + 8 * (a & 1));
+            S2[a][0] = v4.x;
+            S2[a][1] = v4.y;
+            S2[a][2] = v4.z;
+            S2[a][3] = v4.w;
+        }
+    } else {
+#pragma unroll
+        for (int a = 0; a < 8; ++a) S2[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (STATE && len > 0) {
+        float mx = 0.f;
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(S2[a][j]));
+        mx = wave_max(mx);
+        if (mx > 0.f) {
+            int E;
+            frexpf(mx, &E);
+            sigma = (float)(4 - E);
+            const float sc = ldexpf(1.f, 4 - E);
+#pragma unroll
+            for (int a = 0; a < 8; ++a) S2[a] *= sc;
+            mb = mx * sc;
+        }
+    }
+    if (STATE && zero_v) {
+        // both V buffers stay zero (no copies)
+        typedef uint32_t u32x4z __attribute__((ext_vector_type(4)));
+        const u32x4z zz = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int part = 0; part < 2; ++part) lds_st(sm, OFF_VR + (uint32_t)(2048 * w + 1024 * part) + 16 * lane, zz);
+    }
+    for (int idx = tid; idx < 16 * 16; idx += NT) {
+        const int o = (16 + (idx >> 4)) * C + (idx & 15);
+        sm.tT[0][o] = sm.tT[1][o] = (_Float16)0.f;
+        sm.pT[0][o] = sm.pT[1][o] = (_Float16)0.f;
+    }
+
+    Chunk cur;
+    cur.t0 = 0;
+    cur.ne = P.emit_begin[r];
+    cur.lc = len > 0 ? chunk_len(P, len, 0, cur.ne, ne_end) : 0;
+    Chunk nx = next_chunk(P, cur, len, ne_end);
+    Pref pf;
+    floatx4 a10t = {0.f, 0.f, 0.f, 0.f};
+    int vb = 0;
+    if (KEY && cur.lc > 0) {
+        if (!zero_v) dma_v2(sm_lds, 0, G, cur.t0, cur.lc, L2, lane, w);
+        load_kq<0>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
+        load_kq<1, WANT_O>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    lds_barrier();
+    if (cur.lc > 0) {
+        if (KEY) key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
+        lds_barrier();
+        if (KEY && nx.lc > 0) {
+            load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
+            load_kq<1, WANT_O>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
+        }
+        if (KEY) key_side_tasks<WANT_O, NORM_Q, false>(sm, 0, w, L, a10t);
+    }
+
+    int p = 0;
+    while (cur.lc > 0) {
+        const Chunk nx2 = next_chunk(P, nx, len, ne_end);
+        const bool has2 = nx2.lc > 0;
+        const int kt2 = has2 ? nx2.t0 : cur.t0;
+        const int klc2 = has2 ? nx2.lc : cur.lc;
+        // the key-side waves' copies have landed (the state waves issue no loads)
+        if (KEY) __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();  // key-side tasks of `cur` complete; previous state step done
+        const int lc = cur.lc;
+        const uint32_t kbuf = OFF_KH + p * KBUF;
+        const uint32_t cwb = OFF_CW + (uint32_t)(w * 4 * C * 4);  // this wave's coefficient rows
+        if (KEY && nx.lc > 0) key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
+        if (KEY) {
+            load_owned<WANT_O, w>(sm_lds, G, kt2, klc2, L);
+            load_kq<1, false>(pf, sm_lds, G, kt2, klc2, w, L);  // gates of `nx2`
+        }
+        floatx4 Y2[2], Z2[2];
+        int eB = 0;
+        if (STATE) {
+            // Y = K^ S2^T, Z^T = S2 Q^T: all fragments first, so that the reads overlap
+            half8 kf[2][4], qf[2][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    kf[tb][m] = lds_ld<half8>(sm, kbuf + L2.yz + 16 * KROWB * tb + 64 * m);
+                    if (WANT_O) qf[tb][m] = lds_ld<half8>(sm, kbuf + 2 * KBUF + L2.yz + 16 * KROWB * tb + 64 * m);
+                }
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) Y2[tb] = Z2[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const half8 sf = cat(h4(S2[2 * m]), h4(S2[2 * m + 1]));
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    Y2[tb] = mfma16(kf[tb][m], sf, Y2[tb]);
+                    if (WANT_O) Z2[tb] = mfma16(sf, qf[tb][m], Z2[tb]);
+                }
+            }
+            const float isg = exp2_(-sigma);
+            float *cwl = sm.cw[w][0];
+            if (lane < 32) {
+                const float e = sm.eg[p][lane];
+                const float kst = sm.ks[p][lane];
+                const float kq = sm.kq[p][lane];
+                cwl[lane] = e * isg * kst;       // B~ = v - cw0 Y'
+                if (WANT_O) cwl[C + lane] = kq * e * isg;  // o (state part) = cw1 Z
+                cwl[2 * C + lane] = sm.ws[p][lane] * exp2_(sigma - sm.gl[p][C - 1]) * kst;  // W' = cw2 U
+                if (WANT_O && !NORM_Q) cwl[3 * C + lane] = kq;  // o (intra part) = cw3 (P U')
+            }
+            // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
+            float bm = 0.f;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const i16x4_t vv = tr4u(sm, OFF_VR + (uint32_t)(vb * V2BUF) + 2048 * tb + L2.vrd);
+                const float4 c4 = lds_ld<float4>(sm, cwb + 4 * (16 * tb + 4 * g));
+                const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x = bf((uint16_t)vv[j]) - cc[j] * Y2[tb][j];
+                    Y2[tb][j] = x;
+                    bm = fmaxf(bm, fabsf(x));
+                }
+            }
+            if (out_of_band(bm)) eB = f16_adjust(wave_max(bm));
+            if (eB != 0) {
+                const float sc = ldexpf(1.f, eB);
+                Y2[0] *= sc;
+                Y2[1] *= sc;
+            }
+        }
+        if (KEY && w == 3) {
+            __builtin_amdgcn_s_setprio(2);
+            key_side_combine(sm, p, L, a10t);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        lds_barrier();  // T of `cur` and the keys of `nx` are complete
+        if (KEY) {
+            // V of `nx` into the other buffer (last read by the B~ of the previous chunk)
+            if (!zero_v && w == 3) {
+                const bool has1 = nx.lc > 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dma_v2(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L2, lane, i);
+            }
+            if (w != 3) __builtin_amdgcn_s_setprio(1);
+            if (nx.lc > 0) key_side_tasks<WANT_O, NORM_Q, false>(sm, p ^ 1, w, L, a10t);
+            if (w != 3) __builtin_amdgcn_s_setprio(0);
+        }
+        if (STATE) {
+            const half8 th0 = tr_frag2(sm, OFF_TT, 0, L2), th1 = tr_frag2(sm, OFF_TT, 1, L2);
+            const half8 tl0 = tr_frag2(sm, OFF_TT + C * C * 2, 0, L2), tl1 = tr_frag2(sm, OFF_TT + C * C * 2, 1, L2);
+            half8 pf0, pf1;
+            if (WANT_O) {
+                pf0 = tr_frag2(sm, OFF_PT + p * (C * C * 2), 0, L2);
+                pf1 = tr_frag2(sm, OFF_PT + p * (C * C * 2), 1, L2);
+            }
+            const float tsc = sm.tsc;
+            const float gCp = sm.gl[p][C - 1];
+            // U = (T diag(beta)) B~, T as its hi/lo pair
+            const half8 bfr = cat(h4(Y2[0]), h4(Y2[1]));
+            floatx4 U2[2];
+            U2[0] = mfma16(th0, bfr, floatx4{0.f, 0.f, 0.f, 0.f});
+            U2[1] = mfma16(th1, bfr, floatx4{0.f, 0.f, 0.f, 0.f});
+            U2[0] = mfma16(tl0, bfr, U2[0]);
+            U2[1] = mfma16(tl1, bfr, U2[1]);
+            half8 ktf[8];
+#pragma unroll
+            for (int a = 0; a < 8; ++a) {
+                const uint32_t co = 64 * (a >> 1) + 8 * (a & 1);
+                ktf[a] = cat(tr4(sm, kbuf + L2.kt[0] + co), tr4(sm, kbuf + L2.kt[1] + co));
+            }
+            float um = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) um = fmaxf(um, fmaxf(fabsf(U2[0][j]), fabsf(U2[1][j])));
+            int eU = 0;
+            if (out_of_band(um)) eU = f16_adjust(wave_max(um));
+            int ets;
+            frexpf(tsc, &ets);
+            const float lus = (float)(ets - 1 - eB);  // u = us U with us = tsc 2^-eB = 2^lus
+
+            // scale of the new state (the rule of the four-wave kernel; a value
+            // column's tokens sit in lanes n, n + 16, n + 32, n + 48)
+            float sig1 = sigma - gCp;
+            float umx = fmaxf(um, __shfl_xor(um, 16));
+            umx = fmaxf(umx, partner32(umx, lane));
+            const float linc = 5.f + log2_(umx) + lus + sig1;
+            const float dmin = fmaxf(sig1 - kSigMax, 0.f);
+            const float mbn = mb * exp2_(-dmin) + exp2_(fminf(linc - dmin, 127.f));
+            float delta = dmin;
+            if (__builtin_amdgcn_ballot_w64(mbn > 0x1p14f) != 0 ||
+                (__builtin_amdgcn_ballot_w64(mbn >= 1.f) == 0 && __builtin_amdgcn_ballot_w64(mbn > 0.f) != 0)) {
+                float mx = 0.f;
+#pragma unroll
+                for (int a = 0; a < 8; ++a)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(S2[a][j]));
+                const float lm = log2_(wave_max(mx)), li = wave_max(linc);
+                const float hi = fmaxf(lm, li), lo = fminf(lm, li);
+                const float ltot = lo > -INFINITY ? hi + log2_(1.f + exp2_(lo - hi)) : hi;
+                delta = fmaxf(floorf(ltot) - 3.f, sig1 - kSigMax);
+                mb = exp2_(ltot - delta);
+            } else {
+                mb = mbn;
+            }
+            sig1 -= delta;
+            const float dsc = exp2_(fminf(-delta, 126.f));
+            const bool scaled = tsc != 1.f || eB != 0 || eU != 0 || delta != 0.f;
+            float *cwl = sm.cw[w][0];
+            if (scaled && lane < 32) {
+                cwl[2 * C + lane] = exp2_(fminf(gCp - sm.gl[p][lane] + sig1 + lus, 126.f)) * sm.ks[p][lane];
+                if (WANT_O) cwl[3 * C + lane] = (NORM_Q ? 1.f : sm.kq[p][lane]) * exp2_(lus - (float)eU);
+            }
+
+            // o^T = cw1 Z^T + cw3 (U'^T P^T): lane holds token 16 tt + n, columns 4 g .. 4 g + 3
+            if (WANT_O) {
+                half8 uf = cat(h4(U2[0]), h4(U2[1]));
+                if (eU != 0) {
+                    const float sc = ldexpf(1.f, eU);
+                    uf = cat(h4(U2[0] * sc), h4(U2[1] * sc));
+                }
+                const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+                const floatx4 PO[2] = {mfma16(uf, pf0, z4), mfma16(uf, pf1, z4)};
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int t = 16 * tt + n;
+                    const float zc = cwl[C + t];
+                    const float pc = (NORM_Q && !scaled) ? 1.f : cwl[3 * C + t];
+                    float ov[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ov[j] = zc * Z2[tt][j] + pc * PO[tt][j];
+                    if (out && t < lc) {
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        typedef __attribute__((address_space(1))) u32x2 gu32x2;
+                        gu32x2 *dst = (gu32x2 *)((gchar *)at_tok(G.o, cur.t0 + t, G.ts) + (16 * w + 4 * g) * 2);
+                        *dst = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
+                    }
+                }
+            }
+            // W' = 2^{sig1} 2^{g_C - g_s} u_s (S2 units), then S2 <- S2 2^{-delta} + K^ T W'
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const float4 s4 = lds_ld<float4>(sm, cwb + 4 * (2 * C + 16 * tb + 4 * g));
+                U2[tb][0] *= s4.x;
+                U2[tb][1] *= s4.y;
+                U2[tb][2] *= s4.z;
+                U2[tb][3] *= s4.w;
+            }
+            const half8 wfr = cat(h4(U2[0]), h4(U2[1]));
+            if (delta != 0.f) {
+#pragma unroll
+                for (int a = 0; a < 8; ++a) S2[a] *= dsc;
+            }
+#pragma unroll
+            for (int a = 0; a < 8; ++a) S2[a] = mfma16(ktf[a], wfr, S2[a]);
+            sigma = sig1;
+
+            if (cur.ne < ne_end && P.emit_after[cur.ne] == cur.t0 + lc)
+                store_state2(P.emit_base + (((int64_t)b * P.M + P.emit_slot[cur.ne]) * H + h) * DV * DK, S2, sigma,
+                             dvr, L2.scol);
+        }
+        cur = nx;
+        nx = nx2;
+        p ^= 1;
+        vb ^= 1;
+    }
+    if (STATE && P.state_dst[r]) store_state2(P.state_dst[r] + (int64_t)h * DV * DK, S2, sigma, dvr, L2.scol);
+}
+
 template <bool WANT_O, bool NORM_Q, bool ALIAS>
 __global__ __launch_bounds__(NT, 2) void chunked_kernel(const LaunchDesc P)
 {
@@ -1475,6 +1877,30 @@ __global__ __launch_bounds__(2 * NT, 2) void chunked8_kernel(const LaunchDesc P)
     }
 }
 
+// Two workgroups of eight waves per (request, head), one per half of d_v
+// (dv2_main); grid 2 x pairs, consecutive blocks the two halves of a pair.
+template <bool WANT_O, bool NORM_Q>
+__device__ __forceinline__ void dv2_dispatch(const LaunchDesc &P, Smem &sm, uint32_t sm_lds) {
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+        case 0: dv2_main<0, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 1: dv2_main<1, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 2: dv2_main<2, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 3: dv2_main<3, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 4: dv2_main<4, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 5: dv2_main<5, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        case 6: dv2_main<6, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+        default: dv2_main<7, WANT_O, NORM_Q>(P, sm, sm_lds); break;
+    }
+}
+template <bool WANT_O, bool NORM_Q>
+__global__ __launch_bounds__(2 * NT, 2) void chunked_dv2_kernel(const LaunchDesc P)
+{
+    __shared__ Smem sm;
+    const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
+    // (work items without outputs run this path with their stores off)
+    dv2_dispatch<WANT_O, NORM_Q>(P, sm, sm_lds);
+}
+
 int cu_count() {
     static const int n = [] {
         int dev = 0, c = 0;
@@ -1504,8 +1930,17 @@ hipError_t launch_chunked(const LaunchDesc &d, int dk, int dv, Elem e, hipStream
     const int nwg = d.nreq * d.H;
     if (nwg == 0) return hipSuccess;
     const bool want_o = d.o != nullptr, norm_q = (d.flags & kNormQ) != 0, alias = (d.flags & kAliasQKV) != 0;
-    // one workgroup per CU or fewer: the eight-wave kernel; otherwise two
-    // four-wave workgroups share a CU
+    // at most half a workgroup per CU: two eight-wave workgroups per pair, one
+    // per half of d_v; one workgroup per CU or fewer: the eight-wave kernel;
+    // otherwise two four-wave workgroups share a CU
+    if (!alias && 2 * nwg <= cu_count()) {
+        const dim3 grid(2 * nwg), block(2 * NT);
+        if (want_o && norm_q) hipLaunchKernelGGL((chunked_dv2_kernel<true, true>), grid, block, 0, s, d);
+        else if (want_o) hipLaunchKernelGGL((chunked_dv2_kernel<true, false>), grid, block, 0, s, d);
+        else if (norm_q) hipLaunchKernelGGL((chunked_dv2_kernel<false, true>), grid, block, 0, s, d);
+        else hipLaunchKernelGGL((chunked_dv2_kernel<false, false>), grid, block, 0, s, d);
+        return hipGetLastError();
+    }
     if (alias) {
         if (want_o && norm_q) launch_variant<true, true, true>(d, nwg, s);
         else if (want_o) launch_variant<true, false, true>(d, nwg, s);

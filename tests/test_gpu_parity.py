@@ -878,11 +878,15 @@ def _heads(w, n):
 
 @pytest.mark.parametrize("op", ["tail", "resume", "prefill"])
 def test_four_and_eight_wave_launches_agree(gdn, op):
-    """A launch with more workgroups than CUs runs the chunked kernel with four
-    waves per workgroup, a smaller one with eight (state and key side on
-    separate waves).  With 300 workgroups the four-wave kernel meets the oracle
-    on sampled pairs (emissions at chunk edges, ragged and empty spans), and
-    heads 0-7 run alone (eight waves) give the same results bit for bit."""
+    """The chunked kernel comes in three launch shapes, chosen by the number of
+    (request, head) pairs against the CUs: more pairs than CUs run four waves
+    per workgroup, two workgroups per CU; up to one pair per CU runs eight
+    waves (state and key side on separate waves); up to half a pair per CU
+    splits each pair's value rows over two eight-wave workgroups.  With 300
+    pairs the four-wave kernel meets the oracle on sampled pairs (emissions at
+    chunk edges, ragged and empty spans); heads 0-63 run alone (192 pairs,
+    eight waves) give the same results bit for bit; heads 0-7 (24 pairs, the
+    split) meet the oracle on every pair."""
     if op == "tail":
         w = W.tail(seed=95, B=3, H=100, d=128, m_list=[700, 1, 333], r_num=10, r_den=100, pad=7)
     elif op == "resume":
@@ -899,16 +903,22 @@ def test_four_and_eight_wave_launches_agree(gdn, op):
     pairs = _sample_pairs(big, 10, 98) + [(0, 5), (big.B - 1, 3)]
     ref = PT.oracle_pairs(big, pairs, init=PT.init_for(big), emit=PT.emit_for(big))
     PT.compare(big, ref, res["state"], res["o"], res.get("ckpt"), label=f"waves-{op}")
-    small = _heads(big, 8)
-    res8 = PT.run_library(gdn, small)
+    nmid = 128 if op == "prefill" else 64  # 256 or 192 pairs: eight waves, one workgroup per pair
+    mid = _heads(big, nmid)
+    res8 = PT.run_library(gdn, mid)
     torch.cuda.synchronize()
-    assert torch.equal(res8["state"], res["state"][:, :8])
+    assert torch.equal(res8["state"], res["state"][:, :nmid])
     spans = PT.spans_of(big)
     for b, (p0, n) in enumerate(spans):
         r0 = big.tok_offset[b] + (p0 - big.first_pos[b])
-        assert torch.equal(res8["o"][r0:r0 + n], res["o"][r0:r0 + n, :8])
+        assert torch.equal(res8["o"][r0:r0 + n], res["o"][r0:r0 + n, :nmid])
     if res.get("ckpt") is not None:
-        assert torch.equal(res8["ckpt"], res["ckpt"][:, :, :8])
+        assert torch.equal(res8["ckpt"], res["ckpt"][:, :, :nmid])
+    small = _heads(big, 8)
+    _log(f"[waves] {small.name} op={op} pairs={small.B * small.H} (value rows split over two workgroups)")
+    r2 = PT.run_library(gdn, small)
+    PT.check_batched(small, {"dv2": (r2["state"], r2["o"], r2.get("ckpt"))}, init=PT.init_for(small),
+                     emit=PT.emit_for(small), label=f"dv2-{op}", log=_log)
 
 
 @pytest.mark.parametrize("B", [2, 10])
