@@ -464,10 +464,68 @@ __device__ __forceinline__ void dma_v_all(uint32_t sm_lds, int vb, const Bases &
 // Keys are kept as stored: a bf16 row is exact in fp16 (8 significant bits)
 // when its elements lie in the fp16 range, and the normalisation 1/||k|| goes
 // into per-token coefficients (ks) instead of being rounded into the row.
-// Converts the 8 columns of one lane (16-byte unit pair of its row) and
-// stores them at LDS byte offset dst (the row's lower unit; the upper one is
-// +16); returns the row's scale s with k^ = s k' (k' the stored fp16 row),
-// 0 for rows past the chunk.
+// A lane converts the 8 columns of one row (16-byte unit pair).  The
+// conversion of a wave's rows is split in three steps so that the rows'
+// latency chains overlap: row_load (unpack, squared norm), the general form
+// for the 4-row blocks that need it (row_general, rare), row_store (fp16 store
+// at LDS byte offset dst, the upper unit at +16; returns the row's scale s
+// with k^ = s k', k' the stored fp16 row, 0 for rows past the chunk).
+struct RowCv {
+    float f[8];
+    float ss;  // squared norm of the row (all 16 lanes of the row)
+};
+__device__ __forceinline__ void row_load(RowCv &r, uint4 raw) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r.f[2 * e] = bflo(wd[e]);
+        r.f[2 * e + 1] = bfhi(wd[e]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16x2v pr = __builtin_bit_cast(bf16x2v, wd[e]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+    }
+    r.ss = row16_sum(ss);  // one token row per 16 lanes
+}
+// A row with ||k|| in [1/2, 2) is stored as it is (unit keys always are).
+// Any other row sends its 4-row block through the general form: each row is
+// scaled by the power of two that brings its largest element into [1/2, 1)
+// (exact), so that it fits fp16 and its squared norm lies in [1/4, d_k]; this
+// also covers squared norms that overflow or underflow float32.  A zero row
+// keeps scale 0 (it stays zero).
+__device__ __forceinline__ bool row_needs_general(const RowCv &r, bool live) {
+    return live && !(r.ss >= 0.25f && r.ss < 4.f);
+}
+__device__ __forceinline__ void row_general(RowCv &r) {
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(r.f[e]));
+    mx = row16_max(mx);
+    const int E = __builtin_amdgcn_frexp_expf(mx);  // mx = m 2^E, m in [1/2, 1)
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        r.f[e] = __builtin_amdgcn_ldexpf(r.f[e], -E);
+        s2 = fmaf(r.f[e], r.f[e], s2);
+    }
+    r.ss = row16_sum(s2);
+}
+__device__ __forceinline__ float row_store(Smem &sm, uint32_t dst, const RowCv &r, bool live) {
+    half4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = (_Float16)r.f[e];
+        hi[e] = (_Float16)r.f[4 + e];
+    }
+    lds_st(sm, dst, lo);
+    lds_st(sm, dst + 16, hi);
+    return (live && r.ss > 0.f) ? __builtin_amdgcn_rsqf(r.ss) : 0.f;
+}
+// The same conversion for one row, in one piece (fewer live registers; the
+// four-wave kernel converts row by row).  Same results as the three steps.
 __device__ __forceinline__ float convert_key_row(Smem &sm, uint32_t dst, uint4 raw, bool live) {
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -519,9 +577,9 @@ __device__ __forceinline__ float convert_key_row(Smem &sm, uint32_t dst, uint4 r
 
 // Queries used as stored (no GDN_NORMALIZE_Q): converts the 8 columns of one
 // lane scaled by the power of two 2^-E that brings the row's largest element
-// into [1/2, 1) (exact), with 2^E returned in kq_out; stored like
-// convert_key_row.  (Normalised queries take convert_key_row: they are kept
-// as stored too, their 1/||q|| going into per-token coefficients.)
+// into [1/2, 1) (exact), with 2^E returned in kq_out; stored like row_store.
+// (Normalised queries take the key steps: they are kept as stored too, their
+// 1/||q|| going into per-token coefficients.)
 __device__ __forceinline__ void convert_query_row_scaled(Smem &sm, uint32_t dst, uint4 raw, bool live,
                                                          float *kq_out) {
     // rows past the chunk hold a copy of a live row (finite); they get scale 0
@@ -555,12 +613,24 @@ __device__ __forceinline__ void convert_query_row_scaled(Smem &sm, uint32_t dst,
 // outputs, of the queries) covers tokens 4 b .. 4 b + 3, lane l converting
 // token 4 b + l/16, columns 8 (l%16) .. +7.  Wave 3, which also finishes T in
 // this phase, and wave 1, which also forms the gate sums, take fewer blocks.
-template <bool WANT_Q>
+// With eight key-side waves (NK = 8, the d_v-split kernel) roles 0-6 convert
+// two or three blocks each (role 1 also forms the gate sums) and role 7,
+// which finishes T in the same phase, none.
+template <bool WANT_Q, int NK = 4>
 __device__ constexpr int cvt_owner(int gi) {  // gi: block gi/2 of keys (gi even) or queries
+    if (NK == 8) {
+        const int kind = WANT_Q ? (gi & 1) : 0, rb = WANT_Q ? (gi >> 1) : gi;
+        return kind == 0 ? (rb < 2 ? 0 : rb < 4 ? 2 : rb - 1)
+                         : (rb < 2 ? 1 : rb == 2 ? 3 : rb < 5 ? 4 : rb < 7 ? 5 : 6);
+    }
     return WANT_Q ? (gi < 5 ? 0 : gi < 10 ? 2 : gi < 13 ? 1 : 3) : (gi >> 1);
 }
 
-template <bool WANT_Q, bool NORM_Q, int W>
+
+// BATCH: the norms of all of the wave's rows before any store (waves that do
+// only key-side work); otherwise row by row (fewer live registers).  Both
+// give the same results.
+template <bool WANT_Q, bool NORM_Q, int W, int NK = 4, bool BATCH = false>
 __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &pf, int lc, const Lane &L,
                                                  uint32_t rawk = OFF_KQR, uint32_t rawq = OFF_KQR + C * DK * 2) {
     const uint32_t kbuf = OFF_KH + pb * KBUF, qbuf = OFF_QH + pb * KBUF;
@@ -570,28 +640,77 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
     uint4 raw[NG];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-        if (cvt_owner<WANT_Q>(gi) != W) continue;
+        if (cvt_owner<WANT_Q, NK>(gi) != W) continue;
         const int kind = WANT_Q ? (gi & 1) : 0;
         const int rb = WANT_Q ? (gi >> 1) : gi;
         raw[gi] = lds_ld<uint4>(sm, (kind ? rawq : rawk) + (uint32_t)(rb * 4 * DK * 2) + 16 * L.lane);
     }
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        if (cvt_owner<WANT_Q>(gi) != W) continue;
+    // keys and normalised queries: a row's norm, the rare general form per
+    // 4-row block, the store; with BATCH the norms of all of the wave's rows
+    // come first, so that their latency chains overlap
+    constexpr bool QN = WANT_Q && NORM_Q;
+    RowCv rc[NG];
+    bool gen[NG];
+    auto load_block = [&](int gi) {
+        const int rb = WANT_Q ? (gi >> 1) : gi;
+        row_load(rc[gi], raw[gi]);
+        gen[gi] = row_needs_general(rc[gi], 4 * rb + L.g < lc);
+    };
+    auto store_block = [&](int gi) {
         const int kind = WANT_Q ? (gi & 1) : 0;
         const int rb = WANT_Q ? (gi >> 1) : gi;
         const int t = 4 * rb + L.g;
         const bool live = t < lc;
         const uint32_t dst = (kind ? qbuf : kbuf) + L.cvt + (uint32_t)(((rb & 3) + 16 * (rb >> 2)) * KROWB);
         if (kind == 0) {
-            const float ksv = convert_key_row(sm, dst, raw[gi], live);
+            const float ksv = row_store(sm, dst, rc[gi], live);
             if (L.n16 == 0) sm.ks[pb][t] = ksv;
         } else {
             // kq: 1/||q'|| of a normalised query, or the power of two of a query used as stored
             float kqv;
-            if (NORM_Q) kqv = convert_key_row(sm, dst, raw[gi], live);
+            if (NORM_Q) kqv = row_store(sm, dst, rc[gi], live);
             else convert_query_row_scaled(sm, dst, raw[gi], live, &kqv);
             if (L.n16 == 0) sm.kq[pb][t] = kqv;
+        }
+    };
+    if (BATCH) {
+        bool any = false;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            if (cvt_owner<WANT_Q, NK>(gi) != W || (WANT_Q && (gi & 1) && !QN)) continue;
+            load_block(gi);
+            any = any || gen[gi];
+        }
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                if (cvt_owner<WANT_Q, NK>(gi) != W || (WANT_Q && (gi & 1) && !QN)) continue;
+                if (__builtin_amdgcn_ballot_w64(gen[gi]) != 0) row_general(rc[gi]);
+            }
+        }
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            if (cvt_owner<WANT_Q, NK>(gi) != W) continue;
+            store_block(gi);
+        }
+    } else {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            if (cvt_owner<WANT_Q, NK>(gi) != W) continue;
+            const int kind = WANT_Q ? (gi & 1) : 0;
+            const int rb = WANT_Q ? (gi >> 1) : gi;
+            const int t = 4 * rb + L.g;
+            const bool live = t < lc;
+            const uint32_t dst = (kind ? qbuf : kbuf) + L.cvt + (uint32_t)(((rb & 3) + 16 * (rb >> 2)) * KROWB);
+            if (kind == 0) {
+                const float ksv = convert_key_row(sm, dst, raw[gi], live);
+                if (L.n16 == 0) sm.ks[pb][t] = ksv;
+            } else {
+                float kqv;
+                if (NORM_Q) kqv = convert_key_row(sm, dst, raw[gi], live);
+                else convert_query_row_scaled(sm, dst, raw[gi], live, &kqv);
+                if (L.n16 == 0) sm.kq[pb][t] = kqv;
+            }
         }
     }
     constexpr int w = W;
@@ -616,13 +735,13 @@ __device__ __forceinline__ void key_side_convert(Smem &sm, int pb, const Pref &p
 // owner map of key_side_convert), for the chunk at span token t0 with lc rows;
 // rows past the chunk are clamped to its last row.  A wave that copies exactly
 // the rows it converts may issue the copies right after its own conversion.
-template <bool WANT_Q, int W>
+template <bool WANT_Q, int W, int NK = 4>
 __device__ __forceinline__ void load_owned(uint32_t sm_lds, const Bases &G, int t0, int lc, const Lane &L) {
     const uint32_t lim = (uint32_t)(lc - 1) * G.ts + L.ldc;
     constexpr int NG = WANT_Q ? 16 : 8;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-        if (cvt_owner<WANT_Q>(gi) != W) continue;
+        if (cvt_owner<WANT_Q, NK>(gi) != W) continue;
         const int kind = WANT_Q ? (gi & 1) : 0;
         const int rb = WANT_Q ? (gi >> 1) : gi;
         dma16(at_tok(kind ? G.q : G.k, t0, G.ts), min((uint32_t)(4 * rb + L.g) * G.ts + L.ldc, lim),
@@ -1123,8 +1242,8 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     lds_barrier();
     if (cur.lc > 0) {
         if (KEY) {
-            if (ALIAS) key_side_convert<WANT_O && !QFROMK, NORM_Q, w>(sm, 0, pf, cur.lc, L, OFF_KQR, OFF_KQR);
-            else key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
+            if (ALIAS) key_side_convert<WANT_O && !QFROMK, NORM_Q, w, 4, SPLIT>(sm, 0, pf, cur.lc, L, OFF_KQR, OFF_KQR);
+            else key_side_convert<WANT_O, NORM_Q, w, 4, SPLIT>(sm, 0, pf, cur.lc, L);
         }
         lds_barrier();  // the raw tiles are free again (ALIAS: tile 0 keeps chunk 0's values)
         if (KEY && nx.lc > 0) {
@@ -1167,9 +1286,9 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         if (KEY && nx.lc > 0) {
             if (ALIAS) {
                 const uint32_t rawn = kp ? OFF_KQR : RAW1;  // raw tile of `nx`
-                key_side_convert<WANT_O && !QFROMK, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L, rawn, rawn);
+                key_side_convert<WANT_O && !QFROMK, NORM_Q, w, 4, SPLIT>(sm, p ^ 1, pf, nx.lc, L, rawn, rawn);
             } else {
-                key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
+                key_side_convert<WANT_O, NORM_Q, w, 4, SPLIT>(sm, p ^ 1, pf, nx.lc, L);
             }
         }
         if (EARLY && KEY) {
@@ -1503,12 +1622,30 @@ __device__ __forceinline__ half8 tr_frag2(const Smem &sm, uint32_t mat, int tt, 
     return cat(tr4(sm, o), tr4(sm, o + 1024));
 }
 
-template <int ROLE, bool WANT_O, bool NORM_Q>
+// Tile tasks of a chunk with NK key-side waves (role kr): tile 0 on role 0,
+// tile 1 on role 2, P on role 1, A_10 on the role that finishes T (kept in
+// its registers for the combine).
+template <bool WANT_O, bool NORM_Q, int NK>
+__device__ __forceinline__ void dv2_key_tasks(Smem &sm, int pb, int kr, const Lane &L, floatx4 &a10t) {
+    if (kr == 1) {
+        if (WANT_O) key_side_P<NORM_Q, false>(sm, pb, L);
+    } else if (kr == NK - 1) {
+        a10t = key_side_a10t(sm, pb, L);
+    } else if (kr == 0 || kr == 2) {
+        bool ill;
+        const floatx4 t = key_side_tile(sm, pb, kr >> 1, L, ill);
+        key_side_tile_out(sm, kr >> 1, t, ill, L);
+    }
+}
+
+template <int ROLE, bool WANT_O, bool NORM_Q, int NK>
 __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t sm_lds)
 {
     constexpr bool STATE = ROLE < 4;
     constexpr bool KEY = ROLE >= 4;
-    constexpr int w = ROLE & 3;
+    constexpr int kr = ROLE - 4;                // key-side role (0 .. NK - 1)
+    constexpr int w = KEY ? (kr & 3) : ROLE;    // lane constants of the four-wave layout
+    constexpr int KC = NK - 1;                  // key-side role that finishes T
 
     const int Lg = xcd_remap(blockIdx.x, gridDim.x);
     const int hv = Lg & 1;
@@ -1602,21 +1739,22 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
     Pref pf;
     floatx4 a10t = {0.f, 0.f, 0.f, 0.f};
     int vb = 0;
+    // each key-side role copies the raw rows it converts (and role 1 the gates)
     if (KEY && cur.lc > 0) {
-        if (!zero_v) dma_v2(sm_lds, 0, G, cur.t0, cur.lc, L2, lane, w);
-        load_kq<0>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
-        load_kq<1, WANT_O>(pf, sm_lds, G, cur.t0, cur.lc, w, L);
+        if (!zero_v && kr < 4) dma_v2(sm_lds, 0, G, cur.t0, cur.lc, L2, lane, kr);
+        load_owned<WANT_O, kr, NK>(sm_lds, G, cur.t0, cur.lc, L);
+        load_kq<1, false>(pf, sm_lds, G, cur.t0, cur.lc, kr == 1 ? 1 : 0, L);
         __builtin_amdgcn_s_waitcnt(0x0F70);
     }
     lds_barrier();
     if (cur.lc > 0) {
-        if (KEY) key_side_convert<WANT_O, NORM_Q, w>(sm, 0, pf, cur.lc, L);
+        if (KEY) key_side_convert<WANT_O, NORM_Q, kr, NK, true>(sm, 0, pf, cur.lc, L);
         lds_barrier();
         if (KEY && nx.lc > 0) {
-            load_kq<0>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
-            load_kq<1, WANT_O>(pf, sm_lds, G, nx.t0, nx.lc, w, L);
+            load_owned<WANT_O, kr, NK>(sm_lds, G, nx.t0, nx.lc, L);
+            load_kq<1, false>(pf, sm_lds, G, nx.t0, nx.lc, kr == 1 ? 1 : 0, L);
         }
-        if (KEY) key_side_tasks<WANT_O, NORM_Q, false>(sm, 0, w, L, a10t);
+        if (KEY) dv2_key_tasks<WANT_O, NORM_Q, NK>(sm, 0, kr, L, a10t);
     }
 
     int p = 0;
@@ -1631,13 +1769,20 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
         const int lc = cur.lc;
         const uint32_t kbuf = OFF_KH + p * KBUF;
         const uint32_t cwb = OFF_CW + (uint32_t)(w * 4 * C * 4);  // this wave's coefficient rows
-        if (KEY && nx.lc > 0) key_side_convert<WANT_O, NORM_Q, w>(sm, p ^ 1, pf, nx.lc, L);
+        // key side of `nx`: conversion, then the raw rows of `nx2` that this
+        // wave converts next (and the gates)
+        if (KEY && nx.lc > 0) key_side_convert<WANT_O, NORM_Q, kr, NK, true>(sm, p ^ 1, pf, nx.lc, L);
         if (KEY) {
-            load_owned<WANT_O, w>(sm_lds, G, kt2, klc2, L);
-            load_kq<1, false>(pf, sm_lds, G, kt2, klc2, w, L);  // gates of `nx2`
+            load_owned<WANT_O, kr, NK>(sm_lds, G, kt2, klc2, L);
+            load_kq<1, false>(pf, sm_lds, G, kt2, klc2, kr == 1 ? 1 : 0, L);  // gates of `nx2`
         }
+
         floatx4 Y2[2], Z2[2];
         int eB = 0;
+        // coefficients of this chunk read back in phase one (rewritten in the
+        // rare scaled case): o = zc Z + pc (P U'), W' = c2 U, and g_C
+        float zc[2], pc[2], gCp;
+        floatx4 c2[2];
         if (STATE) {
             // Y = K^ S2^T, Z^T = S2 Q^T: all fragments first, so that the reads overlap
             half8 kf[2][4], qf[2][4];
@@ -1670,6 +1815,13 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
                 cwl[2 * C + lane] = sm.ws[p][lane] * exp2_(sigma - sm.gl[p][C - 1]) * kst;  // W' = cw2 U
                 if (WANT_O && !NORM_Q) cwl[3 * C + lane] = kq;  // o (intra part) = cw3 (P U')
             }
+            gCp = sm.gl[p][C - 1];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                if (WANT_O) zc[tt] = cwl[C + 16 * tt + n];
+                pc[tt] = (WANT_O && !NORM_Q) ? cwl[3 * C + 16 * tt + n] : 1.f;
+                c2[tt] = lds_ld<floatx4>(sm, cwb + 4 * (2 * C + 16 * tt + 4 * g));
+            }
             // B~ = v - 2^{g_t} S_0 k^_t, in place in Y
             float bm = 0.f;
 #pragma unroll
@@ -1691,7 +1843,7 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
                 Y2[1] *= sc;
             }
         }
-        if (KEY && w == 3) {
+        if (KEY && kr == KC) {
             __builtin_amdgcn_s_setprio(2);
             key_side_combine(sm, p, L, a10t);
             __builtin_amdgcn_s_setprio(0);
@@ -1699,17 +1851,19 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
         lds_barrier();  // T of `cur` and the keys of `nx` are complete
         if (KEY) {
             // V of `nx` into the other buffer (last read by the B~ of the previous chunk)
-            if (!zero_v && w == 3) {
+            if (!zero_v && kr == 3) {
                 const bool has1 = nx.lc > 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     dma_v2(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L2, lane, i);
             }
-            if (w != 3) __builtin_amdgcn_s_setprio(1);
-            if (nx.lc > 0) key_side_tasks<WANT_O, NORM_Q, false>(sm, p ^ 1, w, L, a10t);
-            if (w != 3) __builtin_amdgcn_s_setprio(0);
+            if (kr != KC) __builtin_amdgcn_s_setprio(1);
+            if (nx.lc > 0) dv2_key_tasks<WANT_O, NORM_Q, NK>(sm, p ^ 1, kr, L, a10t);
+            if (kr != KC) __builtin_amdgcn_s_setprio(0);
+
         }
         if (STATE) {
+            const float tsc = sm.tsc;
             const half8 th0 = tr_frag2(sm, OFF_TT, 0, L2), th1 = tr_frag2(sm, OFF_TT, 1, L2);
             const half8 tl0 = tr_frag2(sm, OFF_TT + C * C * 2, 0, L2), tl1 = tr_frag2(sm, OFF_TT + C * C * 2, 1, L2);
             half8 pf0, pf1;
@@ -1717,8 +1871,6 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
                 pf0 = tr_frag2(sm, OFF_PT + p * (C * C * 2), 0, L2);
                 pf1 = tr_frag2(sm, OFF_PT + p * (C * C * 2), 1, L2);
             }
-            const float tsc = sm.tsc;
-            const float gCp = sm.gl[p][C - 1];
             // U = (T diag(beta)) B~, T as its hi/lo pair
             const half8 bfr = cat(h4(Y2[0]), h4(Y2[1]));
             floatx4 U2[2];
@@ -1744,8 +1896,14 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
             // scale of the new state (the rule of the four-wave kernel; a value
             // column's tokens sit in lanes n, n + 16, n + 32, n + 48)
             float sig1 = sigma - gCp;
-            float umx = fmaxf(um, __shfl_xor(um, 16));
-            umx = fmaxf(umx, partner32(umx, lane));
+            float umx;
+            {
+                // maxima over lane pairs (l, l ^ 16), then (l, l ^ 32)
+                const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(um), __float_as_uint(um), false, false);
+                umx = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+                const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(umx), __float_as_uint(umx), false, false);
+                umx = fmaxf(__uint_as_float(b2[0]), __uint_as_float(b2[1]));
+            }
             const float linc = 5.f + log2_(umx) + lus + sig1;
             const float dmin = fmaxf(sig1 - kSigMax, 0.f);
             const float mbn = mb * exp2_(-dmin) + exp2_(fminf(linc - dmin, 127.f));
@@ -1769,9 +1927,16 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
             const float dsc = exp2_(fminf(-delta, 126.f));
             const bool scaled = tsc != 1.f || eB != 0 || eU != 0 || delta != 0.f;
             float *cwl = sm.cw[w][0];
-            if (scaled && lane < 32) {
-                cwl[2 * C + lane] = exp2_(fminf(gCp - sm.gl[p][lane] + sig1 + lus, 126.f)) * sm.ks[p][lane];
-                if (WANT_O) cwl[3 * C + lane] = (NORM_Q ? 1.f : sm.kq[p][lane]) * exp2_(lus - (float)eU);
+            if (scaled) {
+                if (lane < 32) {
+                    cwl[2 * C + lane] = exp2_(fminf(gCp - sm.gl[p][lane] + sig1 + lus, 126.f)) * sm.ks[p][lane];
+                    if (WANT_O) cwl[3 * C + lane] = (NORM_Q ? 1.f : sm.kq[p][lane]) * exp2_(lus - (float)eU);
+                }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    if (WANT_O) pc[tt] = cwl[3 * C + 16 * tt + n];
+                    c2[tt] = lds_ld<floatx4>(sm, cwb + 4 * (2 * C + 16 * tt + 4 * g));
+                }
             }
 
             // o^T = cw1 Z^T + cw3 (U'^T P^T): lane holds token 16 tt + n, columns 4 g .. 4 g + 3
@@ -1786,11 +1951,9 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     const int t = 16 * tt + n;
-                    const float zc = cwl[C + t];
-                    const float pc = (NORM_Q && !scaled) ? 1.f : cwl[3 * C + t];
                     float ov[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ov[j] = zc * Z2[tt][j] + pc * PO[tt][j];
+                    for (int j = 0; j < 4; ++j) ov[j] = zc[tt] * Z2[tt][j] + pc[tt] * PO[tt][j];
                     if (out && t < lc) {
                         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                         typedef __attribute__((address_space(1))) u32x2 gu32x2;
@@ -1800,14 +1963,8 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
                 }
             }
             // W' = 2^{sig1} 2^{g_C - g_s} u_s (S2 units), then S2 <- S2 2^{-delta} + K^ T W'
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const float4 s4 = lds_ld<float4>(sm, cwb + 4 * (2 * C + 16 * tb + 4 * g));
-                U2[tb][0] *= s4.x;
-                U2[tb][1] *= s4.y;
-                U2[tb][2] *= s4.z;
-                U2[tb][3] *= s4.w;
-            }
+            U2[0] *= c2[0];
+            U2[1] *= c2[1];
             const half8 wfr = cat(h4(U2[0]), h4(U2[1]));
             if (delta != 0.f) {
 #pragma unroll
@@ -1879,26 +2036,28 @@ __global__ __launch_bounds__(2 * NT, 2) void chunked8_kernel(const LaunchDesc P)
 
 // Two workgroups of eight waves per (request, head), one per half of d_v
 // (dv2_main); grid 2 x pairs, consecutive blocks the two halves of a pair.
+// Twelve waves: 0-3 the state side, 4-11 the key side (eight roles).
+constexpr int NKV2 = 8;
 template <bool WANT_O, bool NORM_Q>
-__device__ __forceinline__ void dv2_dispatch(const LaunchDesc &P, Smem &sm, uint32_t sm_lds) {
-    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-        case 0: dv2_main<0, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 1: dv2_main<1, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 2: dv2_main<2, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 3: dv2_main<3, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 4: dv2_main<4, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 5: dv2_main<5, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        case 6: dv2_main<6, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-        default: dv2_main<7, WANT_O, NORM_Q>(P, sm, sm_lds); break;
-    }
-}
-template <bool WANT_O, bool NORM_Q>
-__global__ __launch_bounds__(2 * NT, 2) void chunked_dv2_kernel(const LaunchDesc P)
+__global__ __launch_bounds__((4 + NKV2) * 64, 3) void chunked_dv2_kernel(const LaunchDesc P)
 {
     __shared__ Smem sm;
     const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
     // (work items without outputs run this path with their stores off)
-    dv2_dispatch<WANT_O, NORM_Q>(P, sm, sm_lds);
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+        case 0: dv2_main<0, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 1: dv2_main<1, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 2: dv2_main<2, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 3: dv2_main<3, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 4: dv2_main<4, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 5: dv2_main<5, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 6: dv2_main<6, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 7: dv2_main<7, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 8: dv2_main<8, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 9: dv2_main<9, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        case 10: dv2_main<10, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+        default: dv2_main<11, WANT_O, NORM_Q, NKV2>(P, sm, sm_lds); break;
+    }
 }
 
 int cu_count() {
@@ -1934,7 +2093,7 @@ hipError_t launch_chunked(const LaunchDesc &d, int dk, int dv, Elem e, hipStream
     // per half of d_v; one workgroup per CU or fewer: the eight-wave kernel;
     // otherwise two four-wave workgroups share a CU
     if (!alias && 2 * nwg <= cu_count()) {
-        const dim3 grid(2 * nwg), block(2 * NT);
+        const dim3 grid(2 * nwg), block((4 + NKV2) * 64);
         if (want_o && norm_q) hipLaunchKernelGGL((chunked_dv2_kernel<true, true>), grid, block, 0, s, d);
         else if (want_o) hipLaunchKernelGGL((chunked_dv2_kernel<true, false>), grid, block, 0, s, d);
         else if (norm_q) hipLaunchKernelGGL((chunked_dv2_kernel<false, true>), grid, block, 0, s, d);
