@@ -1857,12 +1857,12 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
                 for (int i = 0; i < 4; ++i)
                     dma_v2(sm_lds, vb ^ 1, G, has1 ? nx.t0 : cur.t0, has1 ? nx.lc : cur.lc, L2, lane, i);
             }
-            if (kr != KC) __builtin_amdgcn_s_setprio(1);
             if (nx.lc > 0) dv2_key_tasks<WANT_O, NORM_Q, NK>(sm, p ^ 1, kr, L, a10t);
-            if (kr != KC) __builtin_amdgcn_s_setprio(0);
-
         }
         if (STATE) {
+            // the state chain is the longer side of this phase: it takes issue
+            // priority over the tile tasks (which have slack until the barrier)
+            __builtin_amdgcn_s_setprio(1);
             const float tsc = sm.tsc;
             const half8 th0 = tr_frag2(sm, OFF_TT, 0, L2), th1 = tr_frag2(sm, OFF_TT, 1, L2);
             const half8 tl0 = tr_frag2(sm, OFF_TT + C * C * 2, 0, L2), tl1 = tr_frag2(sm, OFF_TT + C * C * 2, 1, L2);
@@ -1978,6 +1978,7 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
                 store_state2(P.emit_base + (((int64_t)b * P.M + P.emit_slot[cur.ne]) * H + h) * DV * DK, S2, sigma,
                              dvr, L2.scol);
         }
+        if (STATE) __builtin_amdgcn_s_setprio(0);
         cur = nx;
         nx = nx2;
         p ^= 1;
