@@ -310,7 +310,13 @@ def workloads_bench(torch, gdn, W, dev, args):
     nb = (algorithmic_bytes(th, w.B * w.H, w.dk, w.dv, 2)
           + 2 * (th * (2 * w.dk + 2 * 2 + 2 * w.dv) + w.B * w.H * w.dv * w.dk * 4))
     ms = timed(group, reps=5)
-    line(w.name, ms, sum(ks), nb, {"layers": 3, "tokens_are_per_layer": True})
+    line(w.name, ms, sum(ks), nb, {"layers": 3, "tokens_are_per_layer": True, "path": "three calls"})
+    # the same group in one call (one launch: each workgroup takes its pair through the layers)
+    st3 = torch.empty(3, w.B, w.H, w.dv, w.dk, dtype=torch.float32, device=dev)
+    o3 = torch.empty((3,) + tuple(w.v.shape), dtype=w.v.dtype, device=dev)
+    ms = timed(lambda: gdn.tail_replay_group(w.q, w.k, w.v, alphas, betas, w.tok_offset, w.m, w.r_num, w.r_den,
+                                             first_pos=w.first_pos, flags=w.flags, state_out=st3, o=o3), reps=5)
+    line(w.name, ms, sum(ks), nb, {"layers": 3, "tokens_are_per_layer": True, "path": "group call"})
     # prefill with emission, one pass and split
     w = W.named("prefill_emit_B4_H32_N65536", device=dev)
     M = len(w.ckpt_pos[0])

@@ -82,6 +82,10 @@ def load():
     lib.gdn_tail_replay.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p, ctypes.c_int64,
                                     ctypes.c_int64, vp, vp, i64p, vp]
     lib.gdn_tail_replay.restype = ctypes.c_int
+    lib.gdn_tail_replay_group.argtypes = [shp, ctypes.c_int32, vp, vp, vp, ctypes.POINTER(vp),
+                                          ctypes.POINTER(vp), i64p, i64p, i64p, ctypes.c_int64,
+                                          ctypes.c_int64, vp, vp, i64p, vp]
+    lib.gdn_tail_replay_group.restype = ctypes.c_int
     lib.gdn_tail_replay_with_h2d.argtypes = [shp, vp, vp, vp, vp, vp, i64p, i64p, i64p, ctypes.c_int64,
                                              ctypes.c_int64, vp, vp, i64p, vp, vp, ctypes.c_size_t,
                                              vp, vp, vp]
@@ -255,6 +259,36 @@ def tail_replay(q, k, v, alpha, beta, tok_offset, m, r_num, r_den, *, first_pos=
                                   _ptr(v), _ptr(alpha), _ptr(beta), _p64(off), _p64(fp), _p64(mm),
                                   int(r_num), int(r_den), _ptr(state_out), _ptr(o), _p64(kout),
                                   _stream(k.device)))
+    return state_out, o, [int(x) for x in kout]
+
+
+def tail_replay_group(q, k, v, alphas, betas, tok_offset, m, r_num, r_den, *, first_pos=None,
+                      flags=NORMALIZE_K, state_out=None, o=None):
+    """Tail replay of a group of len(alphas) layers chained by identity mixing
+    (layer l + 1's q = k = v is layer l's output), the same span on every layer.
+
+    Returns (state_out [L,B,H,d_v,d_k] float32, o [L,rows,H,d_v], k_b list)."""
+    L = len(alphas)
+    if len(betas) != L:
+        raise ValueError("one beta per alpha")
+    rows, H, dk, dv, dt = _check_tensors(q, k, v, alphas[0], betas[0], None)
+    for a_, b_ in zip(alphas, betas):
+        _check_tensors(None, k, v, a_, b_, None)
+    if o is None:
+        o = torch.empty((L,) + tuple(v.shape), dtype=v.dtype, device=v.device)
+    if tuple(o.shape) != (L,) + tuple(v.shape) or o.dtype != v.dtype or not o.is_contiguous():
+        raise ValueError("o must be a contiguous [L, rows, H, d_v] tensor of v's dtype")
+    mm = _i64(m)
+    B = int(mm.size)
+    off, fp = _rows_meta(tok_offset, first_pos, rows, B)
+    state_out = _state(state_out, (L, B, H, dv, dk), k.device, "state_out")
+    kout = np.zeros(B, np.int64)
+    sh = _shape(B, H, dk, dv, dt, flags)
+    pa = (ctypes.c_void_p * L)(*[_ptr(x) for x in alphas])
+    pb = (ctypes.c_void_p * L)(*[_ptr(x) for x in betas])
+    _check(load().gdn_tail_replay_group(ctypes.byref(sh), L, _ptr(q), _ptr(k), _ptr(v), pa, pb, _p64(off),
+                                        _p64(fp), _p64(mm), int(r_num), int(r_den), _ptr(state_out), _ptr(o),
+                                        _p64(kout), _stream(k.device)))
     return state_out, o, [int(x) for x in kout]
 
 

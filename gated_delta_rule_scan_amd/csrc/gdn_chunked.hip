@@ -1113,8 +1113,11 @@ __device__ __forceinline__ void store_o_rows(const Smem &sm, int vbuf, gchar *ob
 // One wave's part of a (request, head).  ROLE is the wave index: it selects
 // the wave's value rows and key-side task, and as a compile-time constant it
 // removes the per-chunk role branches.
-template <int ROLE, bool WANT_O, bool NORM_Q, bool ALIAS, bool SPLIT = false>
-__device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_t sm_lds)
+// GROUP: one layer of a fused group launch, whose tensors and state slot come
+// from lp instead of P (the requests, spans and flags are P's).
+template <int ROLE, bool WANT_O, bool NORM_Q, bool ALIAS, bool SPLIT = false, bool GROUP = false>
+__device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_t sm_lds,
+                                          const GroupLayer lp = GroupLayer{})
 {
     // SPLIT (eight waves): waves 0-3 carry the state chain and waves 4-7 the
     // key side of the same schedule, each under role ROLE % 4; without SPLIT
@@ -1130,7 +1133,10 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
     const int r = Lg / P.H;
     const int b = P.req[r];
     const int H = P.H;
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
+    // in a group launch, per layer: keeps the lane constants from being computed
+    // once for all layers and held across them
+    if (GROUP) asm volatile("" : "+v"(tid));
     constexpr int w = ROLE & 3;
     const Lane L = make_lane(tid, w, H);
     const int lane = L.lane, l32 = L.l32, hi32 = L.hi32;
@@ -1146,12 +1152,12 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         const uint64_t th = (uint64_t)(row0 * H + h);  // token-head index of the span's first token
         G.ts = (uint32_t)(H * DK * 2);
         G.tg = (uint32_t)(H * 2);
-        G.k = uniform64(reinterpret_cast<uint64_t>(P.k) + th * (DK * 2));
-        G.q = uniform64(reinterpret_cast<uint64_t>(P.q) + th * (DK * 2));
-        G.v = uniform64(reinterpret_cast<uint64_t>(P.v) + th * (DV * 2) + 64 * w);
-        G.o = uniform64(reinterpret_cast<uint64_t>(P.o) + th * (DV * 2));
-        G.a = uniform64(reinterpret_cast<uint64_t>(P.alpha) + th * 2);
-        G.b = uniform64(reinterpret_cast<uint64_t>(P.beta) + th * 2);
+        G.k = uniform64(reinterpret_cast<uint64_t>(GROUP ? lp.k : P.k) + th * (DK * 2));
+        G.q = uniform64(reinterpret_cast<uint64_t>(GROUP ? lp.q : P.q) + th * (DK * 2));
+        G.v = uniform64(reinterpret_cast<uint64_t>(GROUP ? lp.v : P.v) + th * (DV * 2) + 64 * w);
+        G.o = uniform64(reinterpret_cast<uint64_t>(GROUP ? lp.o : P.o) + th * (DV * 2));
+        G.a = uniform64(reinterpret_cast<uint64_t>(GROUP ? lp.alpha : P.alpha) + th * 2);
+        G.b = uniform64(reinterpret_cast<uint64_t>(GROUP ? lp.beta : P.beta) + th * 2);
     }
 
     // ---- state S^T = 2^{-sigma} Sacc: tile a covers d_k rows 32a..32a+31; the
@@ -1543,7 +1549,8 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         lds_barrier();  // the last staged outputs are complete
         if (STATE) store_o_rows(sm, vb_pend, obase_pend, lc_pend, G.ts, w, L);
     }
-    if (STATE && P.state_dst[r]) store_state(P.state_dst[r] + (int64_t)h * DV * DK, Sacc, sigma, w, l32, hi32);
+    if (STATE && P.state_dst[r])
+        store_state(P.state_dst[r] + (GROUP ? lp.state_shift : 0) + (int64_t)h * DV * DK, Sacc, sigma, w, l32, hi32);
 }
 
 // ---- d_v in two halves --------------------------------------------------------
@@ -2035,6 +2042,52 @@ __global__ __launch_bounds__(2 * NT, 2) void chunked8_kernel(const LaunchDesc P)
     }
 }
 
+// A group of layers in one launch (identity mixing: layer l + 1 reads layer l's
+// outputs as its q = k = v, on the same span).  Each workgroup takes its
+// (request, head) through the layers in turn with the four-wave schedule, so
+// that results are bit for bit those of one launch per layer; a workgroup that
+// finishes a layer starts the next one without waiting for the rest of the
+// grid.  Between layers every wave's output stores complete (workgroup-scope
+// release, barrier, acquire) before any wave copies them back as the next
+// layer's rows: the rows of a (request, head) are written and read by the same
+// workgroup, through the same CU's caches and L2 (a device-scope fence, which
+// writes back L2, made the launch 15% slower).
+template <bool NORM_Q>
+__global__ __launch_bounds__(NT, 2) void chunked_group_kernel(const LaunchDesc P, const GroupPtrs gp)
+{
+    __shared__ Smem sm;
+    const uint32_t sm_lds = (uint32_t)reinterpret_cast<uintptr_t>((lvoid_t *)&sm);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int l = 0; l < gp.L; ++l) {
+        // constant indices (a dynamic index into the arguments would copy them to scratch)
+        GroupLayer lp;
+        switch (l) {
+            case 0: lp = gp.layer[0]; break;
+            case 1: lp = gp.layer[1]; break;
+            case 2: lp = gp.layer[2]; break;
+            default: lp = gp.layer[kMaxGroupLayers - 1]; break;
+        }
+        if (l == 0) {
+            switch (wv) {
+                case 0: wave_main<0, true, NORM_Q, false, false, true>(P, sm, sm_lds, lp); break;
+                case 1: wave_main<1, true, NORM_Q, false, false, true>(P, sm, sm_lds, lp); break;
+                case 2: wave_main<2, true, NORM_Q, false, false, true>(P, sm, sm_lds, lp); break;
+                default: wave_main<3, true, NORM_Q, false, false, true>(P, sm, sm_lds, lp); break;
+            }
+        } else {
+            switch (wv) {
+                case 0: wave_main<0, true, NORM_Q, true, false, true>(P, sm, sm_lds, lp); break;
+                case 1: wave_main<1, true, NORM_Q, true, false, true>(P, sm, sm_lds, lp); break;
+                case 2: wave_main<2, true, NORM_Q, true, false, true>(P, sm, sm_lds, lp); break;
+                default: wave_main<3, true, NORM_Q, true, false, true>(P, sm, sm_lds, lp); break;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+}
+
 // Two workgroups of eight waves per (request, head), one per half of d_v
 // (dv2_main); grid 2 x pairs, consecutive blocks the two halves of a pair.
 // Twelve waves: 0-3 the state side, 4-11 the key side (eight roles).
@@ -2080,6 +2133,16 @@ void launch_variant(const LaunchDesc &d, int nwg, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_chunked_group(const LaunchDesc &d, const GroupPtrs &g, hipStream_t s) {
+    const int nwg = d.nreq * d.H;
+    // only where one launch per layer would run the four-wave kernel on every
+    // layer (the results are then the same bits)
+    if (g.L < 1 || g.L > kMaxGroupLayers || nwg <= cu_count() || d.o == nullptr) return hipErrorNotSupported;
+    if (d.flags & kNormQ) hipLaunchKernelGGL((chunked_group_kernel<true>), dim3(nwg), dim3(NT), 0, s, d, g);
+    else hipLaunchKernelGGL((chunked_group_kernel<false>), dim3(nwg), dim3(NT), 0, s, d, g);
+    return hipGetLastError();
+}
 
 bool chunked_supported(int dk, int dv, Elem e) {
     return dk == DK && dv == DV && e == Elem::BF16;

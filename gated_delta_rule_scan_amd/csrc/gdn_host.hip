@@ -235,35 +235,45 @@ gdn_status validate(const gdn_shape *s, const void *q, const void *k, const void
 
 // Queue the launches of a validated call (several when the work items or
 // their emissions exceed one descriptor).
+// Packs the requests from work[i] on into d, as many as one launch takes (d.nreq);
+// returns the index of the first request left for the next launch.
+size_t pack_launch(gdn::LaunchDesc &d, const std::vector<Work> &work, size_t i) {
+    int nreq = 0, nemit = 0;
+    d.emit_begin[0] = 0;
+    while (i < work.size() && nreq < gdn::kMaxReqPerLaunch &&
+           nemit + (int)work[i].emits.size() <= gdn::kMaxEmitPerLaunch) {
+        const Work &w = work[i];
+        d.row0[nreq] = w.row0;
+        d.init_off[nreq] = w.init_off;
+        d.len[nreq] = (int32_t)w.len;
+        d.req[nreq] = w.b;
+        d.state_dst[nreq] = w.dst;
+        d.wflags[nreq] = w.wflags;
+        for (const auto &e : w.emits) {
+            d.emit_after[nemit] = e.first;
+            d.emit_slot[nemit] = e.second;
+            ++nemit;
+        }
+        d.emit_begin[nreq + 1] = nemit;
+        ++nreq;
+        ++i;
+    }
+    d.nreq = nreq;
+    return i;
+}
+
+hipError_t launch_one(const gdn_shape *s, const Plan &plan, hipStream_t stream) {
+    return plan.chunked ? gdn::launch_chunked(plan.d, s->dk, s->dv, plan.elem, stream)
+                        : gdn::launch_recurrent(plan.d, s->dk, s->dv, plan.elem, stream);
+}
+
 gdn_status launch(const gdn_shape *s, Plan &plan, const std::vector<Work> &work, hipStream_t stream) {
-    gdn::LaunchDesc &d = plan.d;
     size_t i = 0;
     while (i < work.size()) {
-        int nreq = 0, nemit = 0;
-        d.emit_begin[0] = 0;
-        while (i < work.size() && nreq < gdn::kMaxReqPerLaunch &&
-               nemit + (int)work[i].emits.size() <= gdn::kMaxEmitPerLaunch) {
-            const Work &w = work[i];
-            d.row0[nreq] = w.row0;
-            d.init_off[nreq] = w.init_off;
-            d.len[nreq] = (int32_t)w.len;
-            d.req[nreq] = w.b;
-            d.state_dst[nreq] = w.dst;
-            d.wflags[nreq] = w.wflags;
-            for (const auto &e : w.emits) {
-                d.emit_after[nemit] = e.first;
-                d.emit_slot[nemit] = e.second;
-                ++nemit;
-            }
-            d.emit_begin[nreq + 1] = nemit;
-            ++nreq;
-            ++i;
-        }
-        if (nreq == 0)  // cannot happen: one request never exceeds the emission budget
+        i = pack_launch(plan.d, work, i);
+        if (plan.d.nreq == 0)  // cannot happen: one request never exceeds the emission budget
             return fail(GDN_ERR_UNSUPPORTED, "emission list does not fit one launch");
-        d.nreq = nreq;
-        hipError_t err = plan.chunked ? gdn::launch_chunked(d, s->dk, s->dv, plan.elem, stream)
-                                      : gdn::launch_recurrent(d, s->dk, s->dv, plan.elem, stream);
+        const hipError_t err = launch_one(s, plan, stream);
         if (err != hipSuccess)
             return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     }
@@ -374,6 +384,71 @@ GDN_API gdn_status gdn_tail_replay(const gdn_shape *shape, const void *q, const 
     if (st == GDN_OK && h_k_out)
         for (int32_t b = 0; b < shape->B; ++b) h_k_out[b] = ks[b];
     return st;
+}
+
+GDN_API gdn_status gdn_tail_replay_group(const gdn_shape *shape, int32_t L, const void *q, const void *k,
+                                         const void *v, const void *const *alpha, const void *const *beta,
+                                         const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                                         const int64_t *h_m, int64_t r_num, int64_t r_den, float *state_out,
+                                         void *o, int64_t *h_k_out, hipStream_t stream) {
+    g_last_error.clear();
+    if (L < 1 || L > gdn::kMaxGroupLayers)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "L = %d layers, 1..%d supported", L, gdn::kMaxGroupLayers);
+    if (!alpha || !beta) return fail(GDN_ERR_INVALID_ARGUMENT, "alpha and beta (host arrays of L pointers) are NULL");
+    std::vector<Work> work;
+    std::vector<int64_t> ks;
+    gdn_status st = prepare_tail(shape, h_tok_offset, h_first_pos, h_m, r_num, r_den, work, ks);
+    if (st != GDN_OK || shape->B == 0) return st;
+    if (shape->dk != shape->dv)
+        return fail(GDN_ERR_UNSUPPORTED, "a group feeds each layer's outputs to the next as q = k = v: d_k = d_v "
+                                         "needed (got %d, %d)", shape->dk, shape->dv);
+    if (!o) return fail(GDN_ERR_INVALID_ARGUMENT, "o is NULL (each layer's outputs are the next layer's inputs)");
+    if (!state_out) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out is NULL");
+    const int64_t rows = h_tok_offset[shape->B];
+    const size_t esz = shape->dtype == GDN_DTYPE_F32 ? 4 : 2;
+    const size_t oslab = (size_t)rows * shape->H * shape->dv * esz;                   // bytes per layer
+    const int64_t sslab = (int64_t)shape->B * shape->H * shape->dv * shape->dk;      // floats per layer
+    if (ranges_overlap(o, (size_t)L * oslab, state_out, (size_t)L * sslab * sizeof(float)))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "o and state_out overlap");
+    auto o_of = [&](int32_t l) { return static_cast<void *>(static_cast<char *>(o) + (size_t)l * oslab); };
+    // layer l: its own state slab; q = k = v = the outputs of layer l - 1
+    std::vector<Plan> plans((size_t)L);
+    std::vector<std::vector<Work>> lw((size_t)L, work);
+    for (int32_t l = 0; l < L; ++l) {
+        if ((st = set_state_out(lw[(size_t)l], state_out + (int64_t)l * sslab, shape)) != GDN_OK) return st;
+        const void *ql = l ? o_of(l - 1) : q, *kl = l ? o_of(l - 1) : k, *vl = l ? o_of(l - 1) : v;
+        if ((st = validate(shape, ql, kl, vl, alpha[l], beta[l], o_of(l), nullptr, nullptr, 0, lw[(size_t)l],
+                           &plans[(size_t)l])) != GDN_OK)
+            return st;
+    }
+    bool all_chunked = true;
+    for (const Plan &pl : plans) all_chunked = all_chunked && pl.chunked;
+    size_t i = 0;
+    while (i < work.size()) {
+        size_t next = i;
+        for (int32_t l = 0; l < L; ++l) next = pack_launch(plans[(size_t)l].d, lw[(size_t)l], i);
+        i = next;
+        // one launch for every layer of these requests where it gives the same
+        // bits as one launch per layer; otherwise one launch per layer
+        hipError_t err = hipErrorNotSupported;
+        if (all_chunked) {
+            gdn::GroupPtrs g{};
+            g.L = L;
+            for (int32_t l = 0; l < L; ++l) {
+                const gdn::LaunchDesc &dl = plans[(size_t)l].d;
+                g.layer[l] = gdn::GroupLayer{dl.q, dl.k, dl.v, dl.alpha, dl.beta, dl.o, (int64_t)l * sslab};
+            }
+            err = gdn::launch_chunked_group(plans[0].d, g, stream);
+        }
+        if (err == hipErrorNotSupported) {
+            for (int32_t l = 0; l < L && (err = launch_one(shape, plans[(size_t)l], stream)) == hipSuccess; ++l) {
+            }
+        }
+        if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    }
+    if (h_k_out)
+        for (int32_t b = 0; b < shape->B; ++b) h_k_out[b] = ks[b];
+    return GDN_OK;
 }
 
 GDN_API gdn_status gdn_tail_replay_with_h2d(const gdn_shape *shape, const void *q, const void *k,

@@ -67,6 +67,23 @@ hipError_t launch_recurrent(const LaunchDesc &d, int dk, int dv, Elem e, hipStre
 // Chunked matrix-core kernel; returns hipErrorNotSupported when the shape or
 // element type has no chunked variant.
 hipError_t launch_chunked(const LaunchDesc &d, int dk, int dv, Elem e, hipStream_t s);
+
+// A group of layers in one launch of the chunked kernel (bf16, d_k = d_v = 128):
+// layer 0 reads q, k, v; layer l > 0 reads layer l - 1's outputs as its q = k = v.
+constexpr int kMaxGroupLayers = 4;
+struct GroupLayer {
+    const void *q, *k, *v, *alpha, *beta;
+    void *o;
+    int64_t state_shift;  // elements added to every state_dst of the descriptor
+};
+struct GroupPtrs {
+    GroupLayer layer[kMaxGroupLayers];
+    int32_t L;
+};
+static_assert(sizeof(LaunchDesc) + sizeof(GroupPtrs) <= 4096, "kernel arguments must fit 4 KiB");
+// hipErrorNotSupported unless one launch per layer would run the four-wave
+// kernel on every layer (more workgroups than CUs) and o is set.
+hipError_t launch_chunked_group(const LaunchDesc &d, const GroupPtrs &g, hipStream_t s);
 bool chunked_supported(int dk, int dv, Elem e);
 
 // out = a p + c per pair (a, c, out: [d][d] with d_v = d_k = d; p: [d][d]),

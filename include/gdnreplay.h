@@ -140,6 +140,39 @@ gdn_status gdn_tail_replay(const gdn_shape *shape,
                            hipStream_t stream);
 
 /*
+ * Tail replay of a group of L linear-attention layers ([TR] §2.2 step 3: the
+ * tail passes through the group's layers in turn; §2.3: each later layer takes
+ * the earlier layer's outputs), under identity mixing: layer l + 1 (l >= 0)
+ * takes layer l's bf16 / fp32 outputs on the replayed rows as its q = k = v.  Every layer
+ * replays the same span k_b = ceil(r m_b) from zero.  Results are, bit for bit,
+ * those of L calls of gdn_tail_replay chained that way.  Where that sequence
+ * would run the chunked kernel with more workgroups than CUs on every layer, all
+ * layers of a launch's requests run in one launch, each workgroup taking its
+ * (request, head) through the layers in turn.  Otherwise the layers are
+ * launched one after the other.
+ *   L          1..4 layers; needs d_k = d_v
+ *   q, k, v    layer 0's inputs (as for gdn_tail_replay; q non-NULL)
+ *   alpha, beta  host arrays of L device pointers: each layer's gates, laid
+ *              out like the inputs
+ *   state_out  device [L][B][H][d_v][d_k] float32: each layer's state at m_b
+ *   o          device [L][rows][H][d_v] (rows = h_tok_offset[B], the inputs'
+ *              element type): each layer's outputs on the replayed rows (other
+ *              rows are not written); must not overlap state_out
+ *   h_k_out    host [B], nullable: receives k_b
+ * Errors: those of gdn_tail_replay; GDN_ERR_INVALID_ARGUMENT for L outside
+ * 1..4, NULL alpha / beta arrays, a NULL o or state_out, or o overlapping
+ * state_out; GDN_ERR_UNSUPPORTED for d_k != d_v.  All layers are checked
+ * before any launch.
+ */
+gdn_status gdn_tail_replay_group(const gdn_shape *shape, int32_t L,
+                                 const void *q, const void *k, const void *v,
+                                 const void *const *alpha, const void *const *beta,
+                                 const int64_t *h_tok_offset, const int64_t *h_first_pos,
+                                 const int64_t *h_m, int64_t r_num, int64_t r_den,
+                                 float *state_out, void *o, int64_t *h_k_out,
+                                 hipStream_t stream);
+
+/*
  * Tail replay overlapped with the host-to-device transfer of the attention
  * layers' KV cache ([TR] §2.5, "transfer and replay overlap": the replay needs
  * only the tail inputs, so the KV copy and the replay run on separate streams

@@ -774,6 +774,81 @@ def test_aliased_grouped_layers_time(gdn):
     _log(f"[alias-time] grouped layer (16 x 32 pairs, 3277 tokens): aliased {ta:.3f} ms, separate {ts:.3f} ms")
 
 
+# --- a group of layers in one call ------------------------------------------------
+
+def _chained_layers(gdn, w, L):
+    """L tail_replay calls, layer l + 1 fed layer l's outputs as q = k = v."""
+    alphas = ([w.alpha] + list(w.layer_alpha))[:L]
+    betas = ([w.beta] + list(w.layer_beta))[:L]
+    q, k, v = w.q, w.k, w.v
+    states, outs = [], []
+    for l in range(L):
+        S, O, _ = gdn.tail_replay(q, k, v, alphas[l], betas[l], w.tok_offset, w.m, w.r_num, w.r_den,
+                                  first_pos=w.first_pos, flags=w.flags)
+        states.append(S)
+        outs.append(O)
+        q = k = v = O
+    return alphas, betas, states, outs
+
+
+def _group_case(gdn, w, L, label):
+    alphas, betas, states, outs = _chained_layers(gdn, w, L)
+    S, O, ks = gdn.tail_replay_group(w.q, w.k, w.v, alphas, betas, w.tok_offset, w.m, w.r_num, w.r_den,
+                                     first_pos=w.first_pos, flags=w.flags)
+    torch.cuda.synchronize()
+    spans = PT.spans_of(w)
+    for l in range(L):
+        assert torch.equal(S[l], states[l]), f"{label}: layer {l + 1} state differs from the chained calls"
+        for b, (p0, n) in enumerate(spans):
+            r0 = w.tok_offset[b] + (p0 - w.first_pos[b])
+            assert torch.equal(O[l][r0:r0 + n], outs[l][r0:r0 + n]), f"{label}: layer {l + 1} outputs differ"
+    _log(f"[{label}] {L} layers, {w.B * w.H} pairs: bit for bit the chained calls")
+    return alphas, betas
+
+
+def test_group_call_matches_chained_calls(gdn):
+    """gdn_tail_replay_group on the three-layer grouped workload (512 pairs: one
+    launch for all layers) gives the chained tail_replay calls' states and
+    outputs bit for bit (their parity against the oracle, teacher-forced and
+    free-running, is test_grouped_tail_three_layers); so does a small batch
+    (16 pairs: one launch per layer) and a single layer.  The group call's time
+    is logged against the chained calls'."""
+    w = W.named("tail10_grouped_B16_H32_m32768_L3", device="cuda")
+    alphas, betas = _group_case(gdn, w, 3, "group-512")
+    small = W.tail(seed=131, B=2, H=8, d=128, m_list=[3000, 700], r_num=10, r_den=100, pad=5, layers=3,
+                   device="cuda")
+    _group_case(gdn, small, 3, "group-16")
+    _group_case(gdn, w, 1, "group-512-L1")
+
+    st = torch.empty(3, w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
+    og = torch.empty((3,) + tuple(w.v.shape), dtype=w.v.dtype, device="cuda")
+
+    def group():
+        gdn.tail_replay_group(w.q, w.k, w.v, alphas, betas, w.tok_offset, w.m, w.r_num, w.r_den,
+                              first_pos=w.first_pos, flags=w.flags, state_out=st, o=og)
+
+    def chained():
+        for l in range(3):
+            gdn.tail_replay(w.q if l == 0 else og[l - 1], w.k if l == 0 else og[l - 1],
+                            w.v if l == 0 else og[l - 1], alphas[l], betas[l], w.tok_offset, w.m, w.r_num,
+                            w.r_den, first_pos=w.first_pos, flags=w.flags, state_out=st[l], o=og[l])
+
+    def t(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 10
+
+    tg, tc = t(group), t(chained)
+    _log(f"[group-time] 3 layers, 16 x 32 pairs, 3277 tokens: one launch {tg:.3f} ms, three launches {tc:.3f} ms")
+
+
 # --- chunk boundaries ------------------------------------------------------------
 
 @pytest.mark.parametrize("kernel", ["recurrent", "auto"])

@@ -261,3 +261,38 @@ def test_noalloc_split_prefill_rejects_sizes_beyond_its_scratch(gdn):
     bad = gdn._i64([n + 1])
     assert lib.gdn_prefill_emit_checkpoints_split_noalloc(ctypes.byref(sh), p, p, p, p, p, gdn._p64(off), None,
                                                           gdn._p64(bad), 1, ck, st, p, None) == 1
+
+
+def _call_group(gdn, L=3, shape_kw=None, alphas=None, betas=None, state=FAKE, o=FAKE + (1 << 30),
+                arrays=True):
+    lib = gdn.load()
+    sk = dict(B=2, H=2, dk=128, dv=128, dtype=1, flags=1)
+    sk.update(shape_kw or {})
+    sh = gdn._Shape(**sk)
+    off, m = gdn._i64([0, 10, 20]), gdn._i64([10, 10])
+    n = max(L, 1)
+    pa = (ctypes.c_void_p * n)(*(alphas if alphas is not None else [FAKE] * n))
+    pb = (ctypes.c_void_p * n)(*(betas if betas is not None else [FAKE] * n))
+    p = ctypes.c_void_p(FAKE)
+    st = lib.gdn_tail_replay_group(ctypes.byref(sh), L, p, p, p, pa if arrays else None, pb if arrays else None,
+                                   gdn._p64(off), None, gdn._p64(m), 5, 100,
+                                   ctypes.c_void_p(state) if state else None, ctypes.c_void_p(o) if o else None,
+                                   None, None)
+    return st, lib.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(L=0), 1, "L = 0"),
+    (dict(L=5), 1, "L = 5"),
+    (dict(arrays=False), 1, "alpha and beta"),
+    (dict(shape_kw={"dv": 64}), 2, "d_k = d_v"),
+    (dict(o=0), 1, "o is NULL"),
+    (dict(state=0), 1, "state_out is NULL"),
+    (dict(o=FAKE), 1, "overlap"),
+    (dict(alphas=[FAKE, FAKE, None]), 1, "non-NULL"),
+    (dict(betas=[FAKE, FAKE + 1, FAKE]), 1, "aligned"),
+])
+def test_group_argument_errors(gdn, kw, code, needle):
+    """Every layer's arguments are checked before any launch."""
+    st, msg = _call_group(gdn, **kw)
+    assert st == code and needle in msg, (st, msg)
