@@ -356,8 +356,8 @@ def main():
                     help="instead of the headline line, time the tail replay overlapped with a "
                          "host-to-device KV transfer on a second stream, one JSON line per KV size")
     ap.add_argument("--prefill", action="store_true",
-                    help="instead of the headline line, time the prefill with emission (4 x 32 pairs, "
-                         "N = 65536, 16 checkpoints) in one pass and split in three segments")
+                    help="instead of the headline line, time the prefill with emission (4 x 32 and "
+                         "1 x 32 pairs, N = 65536, 16 checkpoints) in one pass and split in three segments")
     ap.add_argument("--workloads", action="store_true",
                     help="instead of the headline line, print one line per headline workload (resume, "
                          "tail 5%%, grouped tail 10%% over three layers, prefill with emission): "
@@ -388,6 +388,8 @@ def main():
         return
     if args.prefill:
         prefill_bench(torch, gdn, W.named("prefill_emit_B4_H32_N65536", device=dev), dev, args)
+        # one request (32 pairs): the split's three segments have the idle CUs to run on
+        prefill_bench(torch, gdn, W.prefill(device=dev, B=1, name="prefill_emit_B1_H32_N65536"), dev, args)
         return
     w = W.named("tail5_B16_H32_m32768", device=dev)
     if args.overlap:
