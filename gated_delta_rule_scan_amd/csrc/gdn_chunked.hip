@@ -1405,8 +1405,9 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         const float tsc = sm.tsc;
         const float gCp = sm.gl[p][C - 1];
         if (!SPLIT) key_phase();
-        // the rest of phase two also goes before the co-resident workgroup's phase one
-        if (!SPLIT) __builtin_amdgcn_s_setprio(1);
+        // the rest of phase two goes first: before the co-resident workgroup's phase
+        // one (four waves), before the key-side waves of the same workgroup (eight)
+        __builtin_amdgcn_s_setprio(1);
 
         // U = (T diag(beta)) B~, T as its hi/lo pair
         floatx16 U = {};
@@ -1539,7 +1540,7 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
             store_state(P.emit_base + (((int64_t)b * P.M + P.emit_slot[cur.ne]) * H + h) * DV * DK, Sacc, sigma,
                         w, l32, hi32);
         }  // STATE
-        if (!SPLIT) __builtin_amdgcn_s_setprio(0);
+        if (STATE) __builtin_amdgcn_s_setprio(0);
         if (SPLIT && !STATE && out) lc_pend = lc;  // the key-side waves pass the same final barrier
         cur = nx;
         nx = nx2;
