@@ -957,7 +957,7 @@ def test_four_and_eight_wave_launches_agree(gdn, op):
     (request, head) pairs against the CUs: more pairs than CUs run four waves
     per workgroup, two workgroups per CU; up to one pair per CU runs eight
     waves (state and key side on separate waves); up to half a pair per CU
-    splits each pair's value rows over two eight-wave workgroups.  With 300
+    splits each pair's value rows over two twelve-wave workgroups.  With 300
     pairs the four-wave kernel meets the oracle on sampled pairs (emissions at
     chunk edges, ragged and empty spans); heads 0-63 run alone (192 pairs,
     eight waves) give the same results bit for bit; heads 0-7 (24 pairs, the
