@@ -615,15 +615,15 @@ __device__ __forceinline__ void convert_query_row_scaled(Smem &sm, uint32_t dst,
 // five blocks each, wave 1 (which also forms the gate sums) four and wave 3
 // (which also finishes T in this phase) two; keys alone go three to waves 0
 // and 2 each, two to wave 1 and none to wave 3.
-// With eight key-side waves (NK = 8, the d_v-split kernel) roles 0-6 convert
-// two or three blocks each (role 1 also forms the gate sums) and role 7,
-// which finishes T in the same phase, none.
+// With eight key-side waves (NK = 8, the d_v-split kernel) roles 0 and 2
+// convert three blocks each, roles 1 and 3-6 two (role 1 also forms the gate
+// sums) and role 7, which finishes T in the same phase, none.
 template <bool WANT_Q, int NK = 4>
 __device__ constexpr int cvt_owner(int gi) {  // gi: block gi/2 of keys (gi even) or queries
     if (NK == 8) {
         const int kind = WANT_Q ? (gi & 1) : 0, rb = WANT_Q ? (gi >> 1) : gi;
         return kind == 0 ? (rb < 2 ? 0 : rb < 4 ? 2 : rb - 1)
-                         : (rb < 2 ? 1 : rb == 2 ? 3 : rb < 5 ? 4 : rb < 7 ? 5 : 6);
+                         : (rb < 2 ? 1 : rb == 2 ? 3 : rb == 3 ? 4 : rb == 4 ? 0 : rb == 5 ? 5 : rb == 6 ? 2 : 6);
     }
     return WANT_Q ? (gi < 5 ? 0 : gi < 10 ? 2 : gi < 14 ? 1 : 3) : (gi < 3 ? 0 : gi < 5 ? 1 : 2);
 }
