@@ -211,6 +211,33 @@ gdn_status validate(const gdn_shape *s, const void *q, const void *k, const void
                     "GDN_KERNEL_CHUNKED: no chunked kernel for d_k = %d, d_v = %d, dtype %d, flags 0x%x "
                     "(it needs bf16, d_k = d_v = 128 and GDN_NORMALIZE_K)",
                     s->dk, s->dv, s->dtype, s->flags);
+    // the kernels write o and the states while they read the inputs: the
+    // span rows of q, k, v, alpha and beta must not share memory with either
+    if (any_tokens) {
+        int64_t r0 = INT64_MAX, r1 = INT64_MIN;
+        for (const Work &w : work)
+            if (w.len > 0) {
+                r0 = std::min(r0, w.row0);
+                r1 = std::max(r1, w.row0 + w.len);
+            }
+        const size_t row = (size_t)s->H * esz;  // bytes of one row per unit of width
+        auto span_of = [&](const void *p, int64_t width) {
+            return std::make_pair(p ? static_cast<const char *>(p) + (size_t)r0 * row * (size_t)width : nullptr,
+                                  (size_t)(r1 - r0) * row * (size_t)width);
+        };
+        const std::pair<const char *, size_t> in[5] = {span_of(q, s->dk), span_of(k, s->dk), span_of(v, s->dv),
+                                                       span_of(alpha, 1), span_of(beta, 1)};
+        const auto out = span_of(o, s->dv);
+        const size_t slot = (size_t)s->H * s->dv * s->dk * sizeof(float);
+        for (const auto &e : in) {
+            if (!e.first) continue;
+            if (out.first && ranges_overlap(out.first, out.second, e.first, e.second))
+                return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps q, k, v, alpha or beta on the span rows");
+            for (const Work &w : work)
+                if (w.dst && ranges_overlap(w.dst, slot, e.first, e.second))
+                    return fail(GDN_ERR_INVALID_ARGUMENT, "a state buffer overlaps q, k, v, alpha or beta");
+        }
+    }
     plan->elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;
     plan->chunked = kern == 1;
 

@@ -42,7 +42,9 @@
  *    null stream) and results are ready when that stream has drained.
  *  - Only the rows of a span are read from q, k, v, alpha, beta; o is written
  *    on the rows of the span only (other rows are left untouched); o == NULL
- *    skips the outputs (q may then be NULL).
+ *    skips the outputs (q may then be NULL).  Neither o nor a state written
+ *    by the call may share memory with the rows of q, k, v, alpha or beta
+ *    between the first and the last span row (GDN_ERR_INVALID_ARGUMENT).
  *  - Thread-safe: calls keep no shared mutable state (the error text is
  *    thread-local).
  *  - Errors: GDN_ERR_INVALID_ARGUMENT / GDN_ERR_UNSUPPORTED are detected on the

@@ -73,6 +73,18 @@ def test_tail_argument_errors(gdn, kw, needle):
     assert st == 1 and needle in msg, msg
 
 
+@pytest.mark.parametrize("kw,needle", [
+    (dict(state=FAKE + (1 << 31)), "o overlaps q, k, v"),                 # o == the inputs
+    (dict(state=FAKE, o=FAKE + (1 << 30)), "state buffer overlaps"),      # state_out == the inputs
+    (dict(state=FAKE + 8192, o=FAKE + (1 << 30)), "state buffer overlaps"),  # starts inside the span rows
+])
+def test_outputs_must_not_overlap_inputs(gdn, kw, needle):
+    """The kernels write o and the states while they read q, k, v, alpha and
+    beta; a call where they share memory is refused before anything is queued."""
+    st, msg = _call_tail(gdn, **kw)
+    assert st == 1 and needle in msg, msg
+
+
 def test_tail_span_outside_stored_tail_rows(gdn):
     # rows hold positions 91..100 of each request; m = 100, r = 20% needs 81..100
     st, msg = _call_tail(gdn, first=[91, 91], m=[100, 100], r_num=20, r_den=100)
@@ -263,7 +275,7 @@ def test_noalloc_split_prefill_rejects_sizes_beyond_its_scratch(gdn):
                                                           gdn._p64(bad), 1, ck, st, p, None) == 1
 
 
-def _call_group(gdn, L=3, shape_kw=None, alphas=None, betas=None, state=FAKE, o=FAKE + (1 << 30),
+def _call_group(gdn, L=3, shape_kw=None, alphas=None, betas=None, state=FAKE + (1 << 31), o=FAKE + (1 << 30),
                 arrays=True):
     lib = gdn.load()
     sk = dict(B=2, H=2, dk=128, dv=128, dtype=1, flags=1)
@@ -288,7 +300,9 @@ def _call_group(gdn, L=3, shape_kw=None, alphas=None, betas=None, state=FAKE, o=
     (dict(shape_kw={"dv": 64}), 2, "d_k = d_v"),
     (dict(o=0), 1, "o is NULL"),
     (dict(state=0), 1, "state_out is NULL"),
-    (dict(o=FAKE), 1, "overlap"),
+    (dict(o=FAKE + (1 << 31)), 1, "o and state_out overlap"),
+    (dict(o=FAKE), 1, "o overlaps q, k, v"),
+    (dict(state=FAKE), 1, "state buffer overlaps"),
     (dict(alphas=[FAKE, FAKE, None]), 1, "non-NULL"),
     (dict(betas=[FAKE, FAKE + 1, FAKE]), 1, "aligned"),
 ])
