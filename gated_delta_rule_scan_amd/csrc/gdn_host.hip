@@ -229,6 +229,8 @@ gdn_status validate(const gdn_shape *s, const void *q, const void *k, const void
                                                        span_of(alpha, 1), span_of(beta, 1)};
         const auto out = span_of(o, s->dv);
         const size_t slot = (size_t)s->H * s->dv * s->dk * sizeof(float);
+        int32_t nb = 0;  // requests covered by the emission store
+        for (const Work &w : work) nb = std::max(nb, w.b + 1);
         for (const auto &e : in) {
             if (!e.first) continue;
             if (out.first && ranges_overlap(out.first, out.second, e.first, e.second))
@@ -236,6 +238,8 @@ gdn_status validate(const gdn_shape *s, const void *q, const void *k, const void
             for (const Work &w : work)
                 if (w.dst && ranges_overlap(w.dst, slot, e.first, e.second))
                     return fail(GDN_ERR_INVALID_ARGUMENT, "a state buffer overlaps q, k, v, alpha or beta");
+            if (emit_base && M > 0 && ranges_overlap(emit_base, (size_t)nb * M * slot, e.first, e.second))
+                return fail(GDN_ERR_INVALID_ARGUMENT, "ckpt_states overlaps q, k, v, alpha or beta");
         }
     }
     plan->elem = s->dtype == GDN_DTYPE_F32 ? gdn::Elem::F32 : gdn::Elem::BF16;

@@ -160,18 +160,27 @@ def test_prefill_errors(gdn):
     p = ctypes.c_void_p(FAKE)
     off = gdn._i64([0, 20])
 
-    def call(pos, first=None, states=FAKE, out=FAKE + 10 ** 9):
+    store = FAKE + (1 << 20)
+
+    def call(pos, first=None, states=store, out=FAKE + 10 ** 9):
         posa = gdn._i64(pos)
-        return lib.gdn_prefill_emit_checkpoints(
+        st = lib.gdn_prefill_emit_checkpoints(
             ctypes.byref(sh), p, p, p, p, p, gdn._p64(off), gdn._p64(gdn._i64(first)),
             gdn._p64(posa), len(pos), ctypes.c_void_p(states) if states else None,
             ctypes.c_void_p(out), None, None)
+        return st, lib.gdn_last_error().decode()
 
-    assert call([5, 21]) == 1                  # beyond N
-    assert call([5, 4]) == 1                   # not increasing
-    assert call([5], first=[2]) == 1           # prefill needs position 1
-    assert call([5], states=0) == 1            # emission store missing
-    assert call([5], out=FAKE) == 1            # state_out overlaps the store
+    def fails(needle, *a, **kw):
+        st, msg = call(*a, **kw)
+        return st == 1 and needle in msg
+
+    assert fails("", [5, 21])                  # beyond N
+    assert fails("increasing", [5, 4])         # not increasing
+    assert fails("", [5], first=[2])           # prefill needs position 1
+    assert fails("", [5], states=0)            # emission store missing
+    assert fails("overlap", [5], out=store)    # state_out overlaps the store
+    # the emission store is written while the input rows are read (20 rows x 16 fp32 = 1280 B)
+    assert fails("ckpt_states overlaps", [5], states=FAKE + 1024)
 
 
 def test_split_prefill_workspace_checks(gdn):
