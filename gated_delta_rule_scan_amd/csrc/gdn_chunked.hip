@@ -65,6 +65,8 @@
 // (which needs no T), the conversion of n + 1 and the last step of T for n;
 // after the second, the tile tasks of n + 1 and the rest of the state chain
 // of n.
+#include <atomic>
+
 #include "gdn_launch.h"
 #include "gdn_numeric.h"
 
@@ -2120,14 +2122,17 @@ __global__ __launch_bounds__((4 + NKV2) * 64, 3) void chunked_dv2_kernel(const L
     }
 }
 
+// CUs of the current device, read once per device (0 if the query fails: every
+// launch then takes the four-wave kernel).
 int cu_count() {
-    static const int n = [] {
-        int dev = 0, c = 0;
-        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        return c;
-    }();
-    return n;
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices] = {};
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices && (c = cached[dev].load(std::memory_order_relaxed)) > 0) return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 0) return 0;
+    if (dev < kMaxDevices) cached[dev].store(c, std::memory_order_relaxed);
+    return c;
 }
 
 template <bool WANT_O, bool NORM_Q, bool ALIAS>
