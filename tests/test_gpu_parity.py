@@ -886,10 +886,13 @@ def test_unnormalised_queries(gdn, kernel, op):
 def test_replays_captured_in_a_graph(gdn):
     """The entry points only validate on the host and queue kernels on the
     caller's stream, so a serving loop can capture them in a HIP graph: a
-    captured chunked tail replay, split prefill and float32 per-token resume,
-    replayed three times with eager work in between, reproduce the eager
-    results bit for bit each time."""
+    captured chunked tail replay, split prefill, float32 per-token resume and
+    two-layer group call (264 pairs: its one-launch form), replayed three
+    times with eager work in between, reproduce the eager results bit for bit
+    each time."""
     wt = W.tail(seed=91, B=2, H=4, m_list=[900, 640], r_num=10, r_den=100, pad=2)
+    wg = W.tail(seed=94, B=2, H=132, d=128, m_list=[700, 400], r_num=10, r_den=100, pad=3, layers=2,
+                device="cuda")
     wr = W.resume(seed=92, B=2, H=2, d=64, N=300, M=3, dtype="f32", depths=[290, 150])
     wp = W.prefill(seed=93, B=1, H=2, d=128, N=1000, M=3, lengths=[1000])
     for w in (wt, wr, wp):
@@ -902,6 +905,9 @@ def test_replays_captured_in_a_graph(gdn):
     st_p = torch.empty(1, 2, 128, 128, device="cuda")
     o_p = torch.empty_like(wp.v)
     ws = torch.empty(gdn.prefill_split_workspace_bytes(1, 2, 128, 128), dtype=torch.uint8, device="cuda")
+    ag, bg = [wg.alpha, wg.layer_alpha[0]], [wg.beta, wg.layer_beta[0]]
+    st_g = torch.empty(2, wg.B, wg.H, 128, 128, device="cuda")
+    o_g = torch.empty((2,) + tuple(wg.v.shape), dtype=wg.v.dtype, device="cuda")
 
     def work():
         gdn.tail_replay(wt.q, wt.k, wt.v, wt.alpha, wt.beta, wt.tok_offset, wt.m, wt.r_num, wt.r_den,
@@ -911,8 +917,10 @@ def test_replays_captured_in_a_graph(gdn):
         gdn.prefill_emit_checkpoints_split(wp.q, wp.k, wp.v, wp.alpha, wp.beta, wp.tok_offset,
                                            wp.ckpt_pos, flags=wp.flags, ckpt_states=cs_p,
                                            state_out=st_p, o=o_p, workspace=ws)
+        gdn.tail_replay_group(wg.q, wg.k, wg.v, ag, bg, wg.tok_offset, wg.m, wg.r_num, wg.r_den,
+                              first_pos=wg.first_pos, flags=wg.flags, state_out=st_g, o=o_g)
 
-    outs = (st_t, o_t, st_r, o_r, cs_p, st_p, o_p)
+    outs = (st_t, o_t, st_r, o_r, cs_p, st_p, o_p, st_g, o_g)
     for t in outs:
         t.zero_()  # o is written on span rows only; the other rows stay zero
     work()
