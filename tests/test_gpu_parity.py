@@ -6,6 +6,7 @@ oracle runs a batch of pairs at a time).  Rows outside every span are
 NaN-poisoned, so any read outside a span shows up as a NaN in the results.
 """
 import os
+import time
 
 import numpy as np
 import pytest
@@ -1007,9 +1008,10 @@ def test_four_and_eight_wave_launches_agree(gdn, op):
 @pytest.mark.parametrize("B", [2, 10])
 @pytest.mark.parametrize("flags", [3, 1])
 def test_runs_are_deterministic(gdn, B, flags):
-    """The same call three times gives the same bits (64 workgroups: the
-    eight-wave chunked kernel; 320: the four-wave one; queries normalised or
-    used as stored).  No reduction or hand-off depends on timing."""
+    """The same call three times gives the same bits (64 pairs: the d_v-split
+    chunked kernel, two workgroups per pair; 320: the four-wave one; queries
+    normalised or used as stored).  No reduction or hand-off depends on
+    timing."""
     w = W.tail(seed=99, B=B, m=3000, r_num=10, r_den=100)
     PT.to_device(w)
     outs = []
@@ -1021,6 +1023,51 @@ def test_runs_are_deterministic(gdn, B, flags):
     for S, O in outs[1:]:
         assert torch.equal(S.view(torch.int32), outs[0][0].view(torch.int32))
         assert torch.equal(O.view(torch.int16), outs[0][1].view(torch.int16))
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_sustained_load_is_bit_identical(gdn):
+    """Back-to-back launches of each chunked launch shape for two seconds (the
+    d_v-split kernel on the resume workload, the eight-wave kernel at 256
+    pairs, the four-wave kernel at 512 and the one-launch three-layer group
+    call): every result equals the first bit for bit, so no hand-off between
+    waves, workgroups or layers depends on timing."""
+    dev = torch.device("cuda")
+    cases = []
+    wr = W.named("resume_B8_H16_N8192", device=dev)
+    sr, orr = torch.zeros(wr.B, wr.H, 128, 128, device=dev), torch.zeros_like(wr.v)
+    cases.append(("resume, d_v split", (sr, orr), lambda: gdn.resume(
+        wr.q, wr.k, wr.v, wr.alpha, wr.beta, wr.tok_offset, wr.ckpt_pos, wr.ckpt_states, wr.depth,
+        first_pos=wr.first_pos, flags=wr.flags, state_out=sr, o=orr)))
+    for B, label in ((8, "tail 256 pairs, eight waves"), (16, "tail 512 pairs, four waves")):
+        wt = W.tail(seed=140 + B, B=B, device=dev)
+        st_, ot = torch.zeros(wt.B, wt.H, 128, 128, device=dev), torch.zeros_like(wt.v)
+        cases.append((label, (st_, ot), lambda wt=wt, st_=st_, ot=ot: gdn.tail_replay(
+            wt.q, wt.k, wt.v, wt.alpha, wt.beta, wt.tok_offset, wt.m, wt.r_num, wt.r_den,
+            first_pos=wt.first_pos, flags=wt.flags, state_out=st_, o=ot)))
+    wg = W.named("tail10_grouped_B16_H32_m32768_L3", device=dev)
+    sg = torch.zeros(3, wg.B, wg.H, 128, 128, device=dev)
+    og = torch.zeros((3,) + tuple(wg.v.shape), dtype=wg.v.dtype, device=dev)
+    ag, bg = [wg.alpha] + list(wg.layer_alpha), [wg.beta] + list(wg.layer_beta)
+    cases.append(("group call, three layers", (sg, og), lambda: gdn.tail_replay_group(
+        wg.q, wg.k, wg.v, ag, bg, wg.tok_offset, wg.m, wg.r_num, wg.r_den, first_pos=wg.first_pos,
+        flags=wg.flags, state_out=sg, o=og)))
+    for label, outs, fn in cases:
+        fn()
+        torch.cuda.synchronize()
+        ref = [_bits(t).clone() for t in outs]
+        n, t0 = 0, time.time()
+        while time.time() - t0 < 2.0:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            n += 5
+            for t, r in zip(outs, ref):
+                assert torch.equal(_bits(t), r), f"{label}: launch {n} differs from the first"
+        _log(f"[sustained] {label}: {n} launches in {time.time() - t0:.1f} s, all bit-identical")
 
 
 # --- accuracy over the domain of the contraction condition ----------------------------
