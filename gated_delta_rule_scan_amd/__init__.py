@@ -193,6 +193,8 @@ def _check_tensors(q, k, v, alpha, beta, o):
             continue
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
+        if t.device != k.device:
+            raise ValueError(f"{name} is on {t.device}, k on {k.device}: one device per call")
         if t.dtype != dt:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {dt}")
         if not t.is_contiguous():
@@ -217,6 +219,8 @@ def _state(t: Optional[torch.Tensor], shape, device, name):
         return torch.empty(shape, dtype=torch.float32, device=device)
     if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must be contiguous float32 of shape {tuple(shape)}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
     return t
 
 
@@ -241,6 +245,13 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _call(device, fn, *args):
+    """Run a library entry point with `device` current (the library reads the
+    current device's properties and its scratch array on that device)."""
+    with torch.cuda.device(device):
+        _check(fn(*args))
+
+
 def tail_replay(q, k, v, alpha, beta, tok_offset, m, r_num, r_den, *, first_pos=None,
                 flags=NORMALIZE_K, state_out=None, o=None, want_o=True):
     """Zero-start replay of the last ceil(r m_b) positions of each request.
@@ -255,10 +266,10 @@ def tail_replay(q, k, v, alpha, beta, tok_offset, m, r_num, r_den, *, first_pos=
     state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
     kout = np.zeros(B, np.int64)
     sh = _shape(B, H, dk, dv, dt, flags)
-    _check(load().gdn_tail_replay(ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k),
-                                  _ptr(v), _ptr(alpha), _ptr(beta), _p64(off), _p64(fp), _p64(mm),
-                                  int(r_num), int(r_den), _ptr(state_out), _ptr(o), _p64(kout),
-                                  _stream(k.device)))
+    _call(k.device, load().gdn_tail_replay,
+        ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _p64(off), _p64(fp), _p64(mm), int(r_num), int(r_den), _ptr(state_out), _ptr(o), _p64(kout),
+        _stream(k.device))
     return state_out, o, [int(x) for x in kout]
 
 
@@ -278,6 +289,8 @@ def tail_replay_group(q, k, v, alphas, betas, tok_offset, m, r_num, r_den, *, fi
         o = torch.empty((L,) + tuple(v.shape), dtype=v.dtype, device=v.device)
     if tuple(o.shape) != (L,) + tuple(v.shape) or o.dtype != v.dtype or not o.is_contiguous():
         raise ValueError("o must be a contiguous [L, rows, H, d_v] tensor of v's dtype")
+    if not o.is_cuda or o.device != k.device:
+        raise ValueError(f"o must be a device tensor on {k.device}")
     mm = _i64(m)
     B = int(mm.size)
     off, fp = _rows_meta(tok_offset, first_pos, rows, B)
@@ -286,9 +299,9 @@ def tail_replay_group(q, k, v, alphas, betas, tok_offset, m, r_num, r_den, *, fi
     sh = _shape(B, H, dk, dv, dt, flags)
     pa = (ctypes.c_void_p * L)(*[_ptr(x) for x in alphas])
     pb = (ctypes.c_void_p * L)(*[_ptr(x) for x in betas])
-    _check(load().gdn_tail_replay_group(ctypes.byref(sh), L, _ptr(q), _ptr(k), _ptr(v), pa, pb, _p64(off),
-                                        _p64(fp), _p64(mm), int(r_num), int(r_den), _ptr(state_out), _ptr(o),
-                                        _p64(kout), _stream(k.device)))
+    _call(k.device, load().gdn_tail_replay_group,
+        ctypes.byref(sh), L, _ptr(q), _ptr(k), _ptr(v), pa, pb, _p64(off), _p64(fp), _p64(mm), int(r_num),
+        int(r_den), _ptr(state_out), _ptr(o), _p64(kout), _stream(k.device))
     return state_out, o, [int(x) for x in kout]
 
 
@@ -315,11 +328,11 @@ def tail_replay_with_h2d(q, k, v, alpha, beta, tok_offset, m, r_num, r_den, kv_s
     state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
     kout = np.zeros(B, np.int64)
     sh = _shape(B, H, dk, dv, dt, flags)
-    _check(load().gdn_tail_replay_with_h2d(
+    _call(k.device, load().gdn_tail_replay_with_h2d,
         ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
         _p64(off), _p64(fp), _p64(mm), int(r_num), int(r_den), _ptr(state_out), _ptr(o), _p64(kout),
         ctypes.c_void_p(kv_dst.data_ptr()), ctypes.c_void_p(kv_src.data_ptr()), nbytes,
-        _stream(k.device), ctypes.c_void_p(copy_stream.cuda_stream), ctypes.c_void_p(copy_done.cuda_event)))
+        _stream(k.device), ctypes.c_void_p(copy_stream.cuda_stream), ctypes.c_void_p(copy_done.cuda_event))
     return state_out, o, [int(x) for x in kout]
 
 
@@ -341,15 +354,15 @@ def resume(q, k, v, alpha, beta, tok_offset, ckpt_pos, ckpt_states, depth, *, fi
         if ckpt_states.dtype != torch.float32 or not ckpt_states.is_contiguous() or \
                 tuple(ckpt_states.shape) != (B, M, H, dv, dk):
             raise ValueError(f"ckpt_states must be contiguous float32 [{B},{M},{H},{dv},{dk}]")
+        if not ckpt_states.is_cuda or ckpt_states.device != k.device:
+            raise ValueError(f"ckpt_states must be a device tensor on {k.device}")
     state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
     jout = np.zeros(B, np.int32)
     sh = _shape(B, H, dk, dv, dt, flags)
-    _check(load().gdn_resume(ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v),
-                             _ptr(alpha), _ptr(beta), _p64(off), _p64(fp),
-                             _p64(pos.reshape(-1)), M, _ptr(ckpt_states), _p64(dd),
-                             _ptr(state_out), _ptr(o),
-                             jout.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                             _stream(k.device)))
+    _call(k.device, load().gdn_resume,
+          ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _p64(off), _p64(fp), _p64(pos.reshape(-1)), M, _ptr(ckpt_states), _p64(dd), _ptr(state_out), _ptr(o),
+        jout.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _stream(k.device))
     return state_out, o, [int(x) for x in jout]
 
 
@@ -370,10 +383,10 @@ def prefill_emit_checkpoints(q, k, v, alpha, beta, tok_offset, ckpt_pos, *, flag
     ckpt_states = _state(ckpt_states, (B, M, H, dv, dk), k.device, "ckpt_states")
     state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
     sh = _shape(B, H, dk, dv, dt, flags)
-    _check(load().gdn_prefill_emit_checkpoints(
+    _call(k.device, load().gdn_prefill_emit_checkpoints,
         ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
-        _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o), _stream(k.device)))
+        _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o), _stream(k.device))
     return ckpt_states, state_out, o
 
 
@@ -404,13 +417,13 @@ def prefill_emit_checkpoints_split(q, k, v, alpha, beta, tok_offset, ckpt_pos, *
     need = int(load().gdn_prefill_split_workspace_bytes(ctypes.byref(sh)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    _check(load().gdn_prefill_emit_checkpoints_split(
+    if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != k.device:
+        raise ValueError(f"workspace must be a contiguous device tensor on {k.device}")
+    _call(k.device, load().gdn_prefill_emit_checkpoints_split,
         ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
         _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(k.device)))
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(k.device))
     return ckpt_states, state_out, o
 
 
@@ -433,8 +446,8 @@ def prefill_emit_checkpoints_split_noalloc(q, k, v, alpha, beta, tok_offset, ckp
     ckpt_states = _state(ckpt_states, (B, M, H, dv, dk), k.device, "ckpt_states")
     state_out = _state(state_out, (B, H, dv, dk), k.device, "state_out")
     sh = _shape(B, H, dk, dv, dt, flags)
-    _check(load().gdn_prefill_emit_checkpoints_split_noalloc(
+    _call(k.device, load().gdn_prefill_emit_checkpoints_split_noalloc,
         ctypes.byref(sh), _ptr(q if o is not None else None), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _p64(off), None, _p64(pos.reshape(-1)), M,
-        _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o), _stream(k.device)))
+        _ptr(ckpt_states) if M > 0 else None, _ptr(state_out), _ptr(o), _stream(k.device))
     return ckpt_states, state_out, o

@@ -1025,6 +1025,31 @@ def test_runs_are_deterministic(gdn, B, flags):
         assert torch.equal(O.view(torch.int16), outs[0][1].view(torch.int16))
 
 
+def test_binding_refuses_host_buffers(gdn):
+    """The C library cannot tell host from device pointers, so the binding
+    refuses an output, state, checkpoint store or workspace that is not on the
+    inputs' device before anything reaches it."""
+    w = W.tail(seed=150, B=2, H=2, m=640, r_num=5, r_den=100, device="cuda")
+    args = (w.q, w.k, w.v, w.alpha, w.beta, w.tok_offset, w.m, w.r_num, w.r_den)
+    with pytest.raises(ValueError, match="device"):
+        gdn.tail_replay(*args, first_pos=w.first_pos, flags=w.flags,
+                        state_out=torch.empty(2, 2, 128, 128))
+    with pytest.raises(ValueError, match="device"):
+        gdn.tail_replay(*args, first_pos=w.first_pos, flags=w.flags, o=torch.empty_like(w.v, device="cpu"))
+    with pytest.raises(ValueError, match="device"):
+        gdn.tail_replay_group(w.q, w.k, w.v, [w.alpha], [w.beta], w.tok_offset, w.m, w.r_num, w.r_den,
+                              first_pos=w.first_pos, flags=w.flags,
+                              o=torch.empty((1,) + tuple(w.v.shape), dtype=w.v.dtype))
+    wp = W.prefill(seed=151, B=1, H=2, d=128, N=300, M=2, device="cuda")
+    with pytest.raises(ValueError, match="device"):
+        gdn.prefill_emit_checkpoints(wp.q, wp.k, wp.v, wp.alpha, wp.beta, wp.tok_offset, wp.ckpt_pos,
+                                     flags=wp.flags, ckpt_states=torch.empty(1, 2, 2, 128, 128))
+    with pytest.raises(ValueError, match="device"):
+        gdn.prefill_emit_checkpoints_split(wp.q, wp.k, wp.v, wp.alpha, wp.beta, wp.tok_offset, wp.ckpt_pos,
+                                           flags=wp.flags, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    torch.cuda.synchronize()
+
+
 def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
