@@ -277,7 +277,10 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 }
 // Lane l copies 16 bytes from base + voff to (LDS base) + 16 l.  Inline
 // assembly with an SGPR base, so that the compiler neither waits for it nor
-// orders LDS accesses of other buffers behind it.
+// orders LDS accesses of other buffers behind it.  The copy takes its LDS
+// address from m0, which the statement sets; the compiler keeps no value of
+// its own in m0 in these kernels (their generated code reads m0 nowhere else),
+// so nothing it relies on is overwritten.
 __device__ __forceinline__ void dma16(uint64_t base, uint32_t voff, uint32_t lds_wave_base) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
