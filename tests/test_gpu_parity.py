@@ -812,7 +812,8 @@ def test_group_call_matches_chained_calls(gdn):
     launch for all layers) gives the chained tail_replay calls' states and
     outputs bit for bit (their parity against the oracle, teacher-forced and
     free-running, is test_grouped_tail_three_layers); so does a small batch
-    (16 pairs: one launch per layer) and a single layer.  The group call's time
+    (16 pairs: one launch per layer), a single layer and four layers (264 and 16
+    pairs).  The group call's time
     is logged against the chained calls'."""
     w = W.named("tail10_grouped_B16_H32_m32768_L3", device="cuda")
     alphas, betas = _group_case(gdn, w, 3, "group-512")
@@ -820,6 +821,13 @@ def test_group_call_matches_chained_calls(gdn):
                    device="cuda")
     _group_case(gdn, small, 3, "group-16")
     _group_case(gdn, w, 1, "group-512-L1")
+    # the most layers one call takes, in the one-launch form (264 pairs) and per layer (16 pairs)
+    four = W.tail(seed=132, B=2, H=132, d=128, m_list=[900, 500], r_num=10, r_den=100, pad=2, layers=4,
+                  device="cuda")
+    _group_case(gdn, four, 4, "group-264-L4")
+    four_small = W.tail(seed=133, B=2, H=8, d=128, m_list=[900, 500], r_num=10, r_den=100, layers=4,
+                        device="cuda")
+    _group_case(gdn, four_small, 4, "group-16-L4")
 
     st = torch.empty(3, w.B, w.H, w.dv, w.dk, dtype=torch.float32, device="cuda")
     og = torch.empty((3,) + tuple(w.v.shape), dtype=w.v.dtype, device="cuda")
