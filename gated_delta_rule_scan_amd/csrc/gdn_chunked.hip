@@ -114,6 +114,7 @@ struct Smem {
     alignas(16) half8 tpart[2][64];      // T_00, T_11^T tiles (accumulator layout) per lane, fp16 hi (0-3) and lo (4-7)
     int tflag[2];                        // tile b: kTileIll (see key_side_tile_out)
     float tsc;                           // 2^{-eT}
+    int tlo;                             // T of the chunk has a lo part (the combine took the hi/lo form)
 };
 constexpr uint32_t OFF_KH = offsetof(Smem, kh);
 constexpr uint32_t OFF_QH = offsetof(Smem, qh);
@@ -1003,7 +1004,10 @@ __device__ __forceinline__ void key_side_combine(Smem &sm, int pb, const Lane &L
     store_tpart(sm, 0, t00, c, rb, ill);
     store_tpart(sm, 1, t10, c, rb, ill);
     store_tpart(sm, 2, t11, c, rb, ill);
-    if (lane == 0) sm.tsc = ldexpf(1.f, -eT);
+    if (lane == 0) {
+        sm.tsc = ldexpf(1.f, -eT);
+        sm.tlo = ill ? 1 : 0;
+    }
 }
 
 // ---- key side, part 3 (wave 1): P -> fp16, transposed -------------------------
@@ -1402,8 +1406,13 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         // operands of `cur` that are complete now are read before the tasks
         const half8 tfr0 = tr_frag_st(sm, OFF_TT, 0, L);
         const half8 tfr1 = tr_frag_st(sm, OFF_TT, 1, L);
-        const half8 tfl0 = tr_frag_st(sm, OFF_TT + C * C * 2, 0, L);  // lo part of T (zero unless refined)
-        const half8 tfl1 = tr_frag_st(sm, OFF_TT + C * C * 2, 1, L);
+        // lo part of T: zero unless the combine took the hi/lo form
+        const bool tlo = sm.tlo != 0;
+        half8 tfl0, tfl1;
+        if (tlo) {
+            tfl0 = tr_frag_st(sm, OFF_TT + C * C * 2, 0, L);
+            tfl1 = tr_frag_st(sm, OFF_TT + C * C * 2, 1, L);
+        }
         half8 pfr0, pfr1;
         if (WANT_O) {
             pfr0 = tr_frag_st(sm, OFF_PT + p * (C * C * 2), 0, L);
@@ -1421,8 +1430,10 @@ __device__ __forceinline__ void wave_main(const LaunchDesc &P, Smem &sm, uint32_
         const half8 yf0 = to_frag(Y, 0), yf1 = to_frag(Y, 1);
         U = mfma32(tfr0, yf0, U);
         U = mfma32(tfr1, yf1, U);
-        U = mfma32(tfl0, yf0, U);
-        U = mfma32(tfl1, yf1, U);
+        if (tlo) {
+            U = mfma32(tfl0, yf0, U);
+            U = mfma32(tfl1, yf1, U);
+        }
         // K^T fragments of the state update
         half8 ktf[4][2];
 #pragma unroll
@@ -1883,7 +1894,12 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
             __builtin_amdgcn_s_setprio(1);
             const float tsc = sm.tsc;
             const half8 th0 = tr_frag2(sm, OFF_TT, 0, L2), th1 = tr_frag2(sm, OFF_TT, 1, L2);
-            const half8 tl0 = tr_frag2(sm, OFF_TT + C * C * 2, 0, L2), tl1 = tr_frag2(sm, OFF_TT + C * C * 2, 1, L2);
+            const bool tlo = sm.tlo != 0;  // T has a lo part (the combine took the hi/lo form)
+            half8 tl0, tl1;
+            if (tlo) {
+                tl0 = tr_frag2(sm, OFF_TT + C * C * 2, 0, L2);
+                tl1 = tr_frag2(sm, OFF_TT + C * C * 2, 1, L2);
+            }
             half8 pf0, pf1;
             if (WANT_O) {
                 pf0 = tr_frag2(sm, OFF_PT + p * (C * C * 2), 0, L2);
@@ -1894,8 +1910,10 @@ __device__ __forceinline__ void dv2_main(const LaunchDesc &P, Smem &sm, uint32_t
             floatx4 U2[2];
             U2[0] = mfma16(th0, bfr, floatx4{0.f, 0.f, 0.f, 0.f});
             U2[1] = mfma16(th1, bfr, floatx4{0.f, 0.f, 0.f, 0.f});
-            U2[0] = mfma16(tl0, bfr, U2[0]);
-            U2[1] = mfma16(tl1, bfr, U2[1]);
+            if (tlo) {
+                U2[0] = mfma16(tl0, bfr, U2[0]);
+                U2[1] = mfma16(tl1, bfr, U2[1]);
+            }
             half8 ktf[8];
 #pragma unroll
             for (int a = 0; a < 8; ++a) {
