@@ -916,8 +916,9 @@ __device__ __forceinline__ void store_tpart(Smem &sm, int blk, const floatx4 &x,
     half4 hi, lo = {0, 0, 0, 0};
     if (split) split16(x, hi, lo);
     else hi = h4(x);
+    // without the split the lo part is not read (the combine's flag in LDS)
 #pragma unroll
-    for (int part = 0; part < 2; ++part) {
+    for (int part = 0; part < (split ? 2 : 1); ++part) {
         _Float16 *tt = sm.tT[part];
         const half4 v = part ? lo : hi;
         if (blk == 0) {
